@@ -1,0 +1,175 @@
+"""Python binding of libfk, the exact batched Lloyd k-means library for MI355X.
+
+Argument marshalling only: shapes, dtypes, data pointers and the stream of
+torch tensors are passed to the C ABI declared in include/fk.h, and a
+non-zero status raises FKError.  Every step of the computation runs in the
+library's HIP kernels; torch only owns the device memory and the stream.
+
+Importing this package loads libfk.so and fails loudly when it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfk.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m exact_lloyd_means_amd.build` "
+        "(or __graft_entry__.build()) first")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+FK_F32, FK_F16, FK_BF16 = 0, 1, 2
+FK_OK, FK_EINVAL, FK_EUNSUPPORTED, FK_EWORKSPACE, FK_EHIP, FK_EHOST = 0, -1, -2, -3, -4, -5
+
+DTYPES = {torch.float32: FK_F32, torch.float16: FK_F16, torch.bfloat16: FK_BF16}
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("d", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_PP = ctypes.POINTER(Problem)
+_SIG = {
+    "fk_abi_version": ([], ctypes.c_int),
+    "fk_status_str": ([ctypes.c_int], ctypes.c_char_p),
+    "fk_last_error": ([], ctypes.c_char_p),
+    "fk_workspace_size": ([_PP, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "fk_centroid_bias": ([_PP, _P, _P, _P], ctypes.c_int),
+    "fk_assign": ([_PP, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "fk_sort_labels": ([_PP, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "fk_update": ([_PP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "fk_lloyd": ([_PP, _P, _P, _P, _P, ctypes.c_int, ctypes.c_float,
+                  ctypes.POINTER(ctypes.c_int), _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "fk_error_count": ([_PP, _P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int64), _P],
+                       ctypes.c_int),
+}
+for _name, (_args, _res) in _SIG.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+
+class FKError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.fk_status_str(status).decode()
+        detail = lib.fk_last_error().decode()
+        super().__init__(f"{where}: {msg}" + (f" ({detail})" if detail else ""))
+
+
+def _check(status: int, where: str) -> None:
+    if status != FK_OK:
+        raise FKError(status, where)
+
+
+def problem(B: int, N: int, K: int, d: int, dtype) -> Problem:
+    code = DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return Problem(B, N, K, d, code, 0)
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libfk must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    return ctypes.c_void_p(int(stream))
+
+
+def _problem_from(X: torch.Tensor, K: int) -> Problem:
+    if X.dim() != 3:
+        raise ValueError("X must be (B, N, d)")
+    B, N, d = X.shape
+    return problem(B, N, K, d, X.dtype)
+
+
+def abi_version() -> int:
+    return lib.fk_abi_version()
+
+
+def workspace_size(p: Problem, chunk_points: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.fk_workspace_size(ctypes.byref(p), chunk_points, ctypes.byref(n)),
+           "fk_workspace_size")
+    return n.value
+
+
+def workspace(p: Problem, device=None, chunk_points: int = 0) -> torch.Tensor:
+    """A caller-owned device workspace of the required size (allocated by torch)."""
+    return torch.empty(workspace_size(p, chunk_points), dtype=torch.uint8,
+                       device=device or "cuda")
+
+
+def fk_centroid_bias(C: torch.Tensor, bias: torch.Tensor, stream=None) -> None:
+    B, K, d = C.shape
+    p = problem(B, 1, K, d, C.dtype)
+    _check(lib.fk_centroid_bias(ctypes.byref(p), _ptr(C), _ptr(bias), _stream(stream)),
+           "fk_centroid_bias")
+
+
+def fk_assign(X: torch.Tensor, C: torch.Tensor, labels: torch.Tensor,
+              min_dist: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+              stream=None) -> None:
+    p = _problem_from(X, C.shape[1])
+    if C.dtype != X.dtype:
+        raise ValueError("C must have the dtype of X")
+    ws = workspace(p, X.device) if ws is None else ws
+    _check(lib.fk_assign(ctypes.byref(p), _ptr(X), _ptr(C), _ptr(labels), _ptr(min_dist),
+                         _ptr(ws), ws.numel(), _stream(stream)), "fk_assign")
+
+
+def fk_sort_labels(labels: torch.Tensor, K: int, counts: torch.Tensor, offsets: torch.Tensor,
+                   sorted_idx: torch.Tensor, ws: torch.Tensor | None = None,
+                   stream=None, d: int = 1, dtype=torch.float32) -> None:
+    B, N = labels.shape
+    p = problem(B, N, K, d, dtype)
+    ws = workspace(p, labels.device) if ws is None else ws
+    _check(lib.fk_sort_labels(ctypes.byref(p), _ptr(labels), _ptr(counts), _ptr(offsets),
+                              _ptr(sorted_idx), _ptr(ws), ws.numel(), _stream(stream)),
+           "fk_sort_labels")
+
+
+def fk_update(X: torch.Tensor, labels: torch.Tensor, C_prev: torch.Tensor, C_next: torch.Tensor,
+              C_next_lowp: torch.Tensor | None, counts: torch.Tensor,
+              ws: torch.Tensor | None = None, stream=None) -> None:
+    p = _problem_from(X, C_prev.shape[1])
+    ws = workspace(p, X.device) if ws is None else ws
+    _check(lib.fk_update(ctypes.byref(p), _ptr(X), _ptr(labels), _ptr(C_prev), _ptr(C_next),
+                         _ptr(C_next_lowp), _ptr(counts), _ptr(ws), ws.numel(),
+                         _stream(stream)), "fk_update")
+
+
+def fk_lloyd(X: torch.Tensor, C: torch.Tensor, labels: torch.Tensor, counts: torch.Tensor,
+             max_iters: int, tol: float = 0.0, want_n_iter: bool = False,
+             ws: torch.Tensor | None = None, stream=None):
+    """Runs Lloyd iterations in place on the fp32 centroids C.  Returns the
+    number of iterations run when want_n_iter (one sync per iteration)."""
+    p = _problem_from(X, C.shape[1])
+    ws = workspace(p, X.device) if ws is None else ws
+    n = ctypes.c_int(0)
+    _check(lib.fk_lloyd(ctypes.byref(p), _ptr(X), _ptr(C), _ptr(labels), _ptr(counts),
+                        int(max_iters), float(tol), ctypes.byref(n) if want_n_iter else None,
+                        _ptr(ws), ws.numel(), _stream(stream)), "fk_lloyd")
+    return n.value if want_n_iter else None
+
+
+def fk_error_count(p: Problem, ws: torch.Tensor, stream=None) -> int:
+    n = ctypes.c_int64(0)
+    _check(lib.fk_error_count(ctypes.byref(p), _ptr(ws), ws.numel(), ctypes.byref(n),
+                              _stream(stream)), "fk_error_count")
+    return n.value

@@ -1,0 +1,310 @@
+// fk_api.hip -- host side of the C ABI declared in include/fk.h: argument
+// checks (before anything is enqueued), workspace layout and kernel sequence
+// of each entry point.  No device memory is allocated here.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "fk_internal.h"
+
+namespace fk {
+hipError_t launch_assign_f16(const void*, const void*, const float*, int32_t*, float*, int64_t,
+                             int64_t, int64_t, int, hipStream_t);
+hipError_t launch_assign_bf16(const void*, const void*, const float*, int32_t*, float*, int64_t,
+                              int64_t, int64_t, int, hipStream_t);
+hipError_t launch_assign_f32(const void*, const void*, const float*, int32_t*, float*, int64_t,
+                             int64_t, int64_t, int, hipStream_t);
+
+hipError_t launch_assign(int dtype, const void* X, const void* C, const float* bias,
+                         int32_t* labels, float* min_dist, int64_t B, int64_t N, int64_t K, int d,
+                         hipStream_t s) {
+    switch (dtype) {
+        case FK_F16: return launch_assign_f16(X, C, bias, labels, min_dist, B, N, K, d, s);
+        case FK_BF16: return launch_assign_bf16(X, C, bias, labels, min_dist, B, N, K, d, s);
+        default: return launch_assign_f32(X, C, bias, labels, min_dist, B, N, K, d, s);
+    }
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Workspace workspace_layout(const fk_problem& p, char* base) {
+    Workspace w{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) -> char* {
+        char* at = base ? base + o : nullptr;
+        o = align256(o + bytes);
+        return at;
+    };
+    const size_t B = (size_t)p.B, N = (size_t)p.N, K = (size_t)p.K, d = (size_t)p.d;
+    w.bias = reinterpret_cast<float*>(take(B * K * sizeof(float)));
+    w.offsets = reinterpret_cast<int32_t*>(take(B * (K + 1) * sizeof(int32_t)));
+    w.cursor = reinterpret_cast<int32_t*>(take(B * K * sizeof(int32_t)));
+    w.sorted_idx = reinterpret_cast<int32_t*>(take(B * N * sizeof(int32_t)));
+    w.sums = reinterpret_cast<float*>(take(B * K * d * sizeof(float)));
+    w.counts = reinterpret_cast<int32_t*>(take(B * K * sizeof(int32_t)));
+    w.lowp = p.dtype == FK_F32 ? nullptr : take(B * K * d * (size_t)dtype_size(p.dtype));
+    w.flags = reinterpret_cast<uint32_t*>(take(256));
+    w.total = o;
+    return w;
+}
+
+}  // namespace fk
+
+namespace {
+
+using namespace fk;
+
+thread_local char g_err[512] = "";
+
+fk_status fail(fk_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+fk_status hip_fail(hipError_t e, const char* what) {
+    return fail(FK_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+#define FK_TRY(call, what)                            \
+    do {                                              \
+        hipError_t fk_e_ = (call);                    \
+        if (fk_e_ != hipSuccess) return hip_fail(fk_e_, what); \
+    } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxIndex = 2147483646;  // N and K must leave room for N + 1 / K + 1 in int32
+constexpr int64_t kMaxD = 65536;
+
+// Largest d the register-resident assign kernel supports for a dtype.
+int64_t max_assign_d(int dtype) { return dtype == FK_F32 ? 256 : 512; }
+
+fk_status check_problem(const fk_problem* p) {
+    if (!p) return fail(FK_EINVAL, "problem is NULL");
+    if (p->B < 1 || p->N < 1 || p->K < 1 || p->d < 1)
+        return fail(FK_EINVAL, "sizes must be >= 1 (B=%lld N=%lld K=%lld d=%lld)", (long long)p->B,
+                    (long long)p->N, (long long)p->K, (long long)p->d);
+    if (p->dtype != FK_F32 && p->dtype != FK_F16 && p->dtype != FK_BF16)
+        return fail(FK_EUNSUPPORTED, "unknown dtype %d", (int)p->dtype);
+    if (p->reserved != 0) return fail(FK_EINVAL, "reserved field must be 0");
+    if (p->N > kMaxIndex || p->K > kMaxIndex)
+        return fail(FK_EUNSUPPORTED, "N and K must be <= %lld", (long long)kMaxIndex);
+    if (p->d > kMaxD) return fail(FK_EUNSUPPORTED, "d must be <= %lld", (long long)kMaxD);
+    if (p->B > 65535) return fail(FK_EUNSUPPORTED, "B must be <= 65535");
+    return FK_OK;
+}
+
+fk_status check_ptr(const void* ptr, const char* name, bool required = true) {
+    if (!ptr) return required ? fail(FK_EINVAL, "%s is NULL", name) : FK_OK;
+    if (!aligned16(ptr)) return fail(FK_EINVAL, "%s is not 16-byte aligned", name);
+    return FK_OK;
+}
+
+fk_status check_ws(const fk_problem& p, void* ws, size_t ws_bytes, Workspace* out) {
+    const Workspace need = workspace_layout(p, nullptr);
+    if (!ws) return fail(FK_EWORKSPACE, "workspace is NULL");
+    if (!aligned16(ws)) return fail(FK_EINVAL, "workspace is not 16-byte aligned");
+    if (ws_bytes < need.total)
+        return fail(FK_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need.total);
+    *out = workspace_layout(p, static_cast<char*>(ws));
+    return FK_OK;
+}
+
+fk_status check_assign_d(const fk_problem& p) {
+    if (p.d > max_assign_d(p.dtype))
+        return fail(FK_EUNSUPPORTED, "assign supports d <= %lld for this dtype (d=%lld)",
+                    (long long)max_assign_d(p.dtype), (long long)p.d);
+    return FK_OK;
+}
+
+#define FK_CHECK(expr)                    \
+    do {                                  \
+        fk_status fk_s_ = (expr);         \
+        if (fk_s_ != FK_OK) return fk_s_; \
+    } while (0)
+
+// Counting-sort argsort of the labels: counts, offsets, cursor, sorted_idx.
+fk_status enqueue_sort(const fk_problem& p, const int32_t* labels, int32_t* counts,
+                       int32_t* offsets, int32_t* cursor, int32_t* sorted_idx, uint32_t* flags,
+                       hipStream_t s) {
+    FK_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(counts), p.B * p.K, 0u, s), "clear counts");
+    FK_TRY(launch_histogram(labels, counts, flags, p.B, p.N, p.K, s), "histogram");
+    FK_TRY(launch_scan(counts, offsets, cursor, p.B, p.K, s), "scan");
+    FK_TRY(launch_scatter(labels, cursor, sorted_idx, p.B, p.N, p.K, s), "scatter");
+    return FK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fk_abi_version(void) { return FK_ABI_VERSION; }
+
+const char* fk_status_str(int status) {
+    switch (status) {
+        case FK_OK: return "FK_OK";
+        case FK_EINVAL: return "FK_EINVAL: invalid argument";
+        case FK_EUNSUPPORTED: return "FK_EUNSUPPORTED: unsupported dtype or size";
+        case FK_EWORKSPACE: return "FK_EWORKSPACE: workspace missing or too small";
+        case FK_EHIP: return "FK_EHIP: HIP runtime or launch failure";
+        case FK_EHOST: return "FK_EHOST: host resource failure";
+        default: return "unknown fk_status";
+    }
+}
+
+const char* fk_last_error(void) { return g_err; }
+
+fk_status fk_workspace_size(const fk_problem* p, int64_t chunk_points, size_t* bytes) {
+    FK_CHECK(check_problem(p));
+    if (!bytes) return fail(FK_EINVAL, "bytes is NULL");
+    if (chunk_points != 0) return fail(FK_EUNSUPPORTED, "streamed workspace not available");
+    *bytes = workspace_layout(*p, nullptr).total;
+    return FK_OK;
+}
+
+fk_status fk_centroid_bias(const fk_problem* p, const void* C, float* bias, void* stream) {
+    FK_CHECK(check_problem(p));
+    FK_CHECK(check_ptr(C, "C"));
+    FK_CHECK(check_ptr(bias, "bias"));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    FK_TRY(launch_centroid_bias(p->dtype, C, bias, p->B * p->K, (int)p->d, s), "centroid bias");
+    return FK_OK;
+}
+
+fk_status fk_assign(const fk_problem* p, const void* X, const void* C, int32_t* labels,
+                    float* min_dist, void* ws, size_t ws_bytes, void* stream) {
+    FK_CHECK(check_problem(p));
+    FK_CHECK(check_ptr(X, "X"));
+    FK_CHECK(check_ptr(C, "C"));
+    FK_CHECK(check_ptr(labels, "labels"));
+    FK_CHECK(check_ptr(min_dist, "min_dist", false));
+    FK_CHECK(check_assign_d(*p));
+    Workspace w;
+    FK_CHECK(check_ws(*p, ws, ws_bytes, &w));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    FK_TRY(launch_centroid_bias(p->dtype, C, w.bias, p->B * p->K, (int)p->d, s), "centroid bias");
+    FK_TRY(launch_assign(p->dtype, X, C, w.bias, labels, min_dist, p->B, p->N, p->K, (int)p->d, s),
+           "assign");
+    return FK_OK;
+}
+
+fk_status fk_sort_labels(const fk_problem* p, const int32_t* labels, int32_t* counts,
+                         int32_t* offsets, int32_t* sorted_idx, void* ws, size_t ws_bytes,
+                         void* stream) {
+    FK_CHECK(check_problem(p));
+    FK_CHECK(check_ptr(labels, "labels"));
+    FK_CHECK(check_ptr(counts, "counts"));
+    FK_CHECK(check_ptr(offsets, "offsets"));
+    FK_CHECK(check_ptr(sorted_idx, "sorted_idx"));
+    Workspace w;
+    FK_CHECK(check_ws(*p, ws, ws_bytes, &w));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    FK_TRY(launch_fill_u32(w.flags, 64, 0u, s), "clear flags");
+    return enqueue_sort(*p, labels, counts, offsets, w.cursor, sorted_idx, w.flags, s);
+}
+
+fk_status fk_update(const fk_problem* p, const void* X, const int32_t* labels,
+                    const float* C_prev, float* C_next, void* C_next_lowp, int32_t* counts,
+                    void* ws, size_t ws_bytes, void* stream) {
+    FK_CHECK(check_problem(p));
+    FK_CHECK(check_ptr(X, "X"));
+    FK_CHECK(check_ptr(labels, "labels"));
+    FK_CHECK(check_ptr(C_prev, "C_prev"));
+    FK_CHECK(check_ptr(C_next, "C_next"));
+    FK_CHECK(check_ptr(C_next_lowp, "C_next_lowp", false));
+    FK_CHECK(check_ptr(counts, "counts"));
+    if (p->dtype == FK_F32 && C_next_lowp && C_next_lowp == static_cast<void*>(C_next))
+        return fail(FK_EINVAL, "C_next_lowp must differ from C_next");
+    if (p->d > 1024) return fail(FK_EUNSUPPORTED, "update supports d <= 1024");
+    Workspace w;
+    FK_CHECK(check_ws(*p, ws, ws_bytes, &w));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t rows = p->B * p->K;
+    FK_TRY(launch_fill_u32(w.flags, 64, 0u, s), "clear flags");
+    FK_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(w.sums), rows * p->d, 0u, s), "clear sums");
+    FK_CHECK(enqueue_sort(*p, labels, counts, w.offsets, w.cursor, w.sorted_idx, w.flags, s));
+    FK_TRY(launch_segment_sums(p->dtype, X, w.sorted_idx, w.offsets, w.sums, p->B, p->N, p->K,
+                               (int)p->d, s),
+           "segment sums");
+    if (p->dtype == FK_F32 && C_next_lowp) {
+        FK_TRY(launch_finalize(p->dtype, w.sums, counts, C_prev, C_next, nullptr, nullptr, nullptr,
+                               rows, (int)p->d, s),
+               "finalize");
+        FK_TRY(hipMemcpyAsync(C_next_lowp, C_next, (size_t)(rows * p->d) * sizeof(float),
+                              hipMemcpyDeviceToDevice, s),
+               "copy fp32 centroids");
+    } else {
+        FK_TRY(launch_finalize(p->dtype, w.sums, counts, C_prev, C_next, C_next_lowp, nullptr,
+                               nullptr, rows, (int)p->d, s),
+               "finalize");
+    }
+    return FK_OK;
+}
+
+fk_status fk_lloyd(const fk_problem* p, const void* X, float* C, int32_t* labels,
+                   int32_t* counts, int max_iters, float tol, int* n_iter, void* ws,
+                   size_t ws_bytes, void* stream) {
+    FK_CHECK(check_problem(p));
+    FK_CHECK(check_ptr(X, "X"));
+    FK_CHECK(check_ptr(C, "C"));
+    FK_CHECK(check_ptr(labels, "labels"));
+    FK_CHECK(check_ptr(counts, "counts"));
+    if (max_iters < 1) return fail(FK_EINVAL, "max_iters must be >= 1");
+    if (!(tol >= 0.f)) return fail(FK_EINVAL, "tol must be >= 0");
+    FK_CHECK(check_assign_d(*p));
+    if (p->d > 1024) return fail(FK_EUNSUPPORTED, "update supports d <= 1024");
+    Workspace w;
+    FK_CHECK(check_ws(*p, ws, ws_bytes, &w));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t rows = p->B * p->K;
+    const bool sync = tol > 0.f || n_iter != nullptr;
+    const void* Cq = p->dtype == FK_F32 ? static_cast<const void*>(C) : w.lowp;
+
+    FK_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(w.sums), rows * p->d, 0u, s), "clear sums");
+    FK_TRY(launch_prepare(p->dtype, C, w.lowp, w.bias, rows, (int)p->d, s), "prepare centroids");
+    int it = 0;
+    while (it < max_iters) {
+        FK_TRY(launch_fill_u32(w.flags, 64, 0u, s), "clear flags");
+        FK_TRY(launch_assign(p->dtype, X, Cq, w.bias, labels, nullptr, p->B, p->N, p->K,
+                             (int)p->d, s),
+               "assign");
+        FK_CHECK(enqueue_sort(*p, labels, counts, w.offsets, w.cursor, w.sorted_idx, w.flags, s));
+        FK_TRY(launch_segment_sums(p->dtype, X, w.sorted_idx, w.offsets, w.sums, p->B, p->N, p->K,
+                                   (int)p->d, s),
+               "segment sums");
+        FK_TRY(launch_finalize(p->dtype, w.sums, counts, C, C, w.lowp, w.bias,
+                               sync ? w.flags + 1 : nullptr, rows, (int)p->d, s),
+               "finalize");
+        ++it;
+        if (sync) {
+            uint32_t bits = 0;
+            FK_TRY(hipMemcpyAsync(&bits, w.flags + 1, sizeof(bits), hipMemcpyDeviceToHost, s),
+                   "read centroid move");
+            FK_TRY(hipStreamSynchronize(s), "synchronise");
+            float move;
+            memcpy(&move, &bits, sizeof(move));
+            if (tol > 0.f && move <= tol) break;
+        }
+    }
+    if (n_iter) *n_iter = it;
+    return FK_OK;
+}
+
+fk_status fk_error_count(const fk_problem* p, const void* ws, size_t ws_bytes, int64_t* count,
+                         void* stream) {
+    FK_CHECK(check_problem(p));
+    if (!count) return fail(FK_EINVAL, "count is NULL");
+    Workspace w;
+    FK_CHECK(check_ws(*p, const_cast<void*>(ws), ws_bytes, &w));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t v = 0;
+    FK_TRY(hipMemcpyAsync(&v, w.flags, sizeof(v), hipMemcpyDeviceToHost, s), "read error count");
+    FK_TRY(hipStreamSynchronize(s), "synchronise");
+    *count = v;
+    return FK_OK;
+}
+
+}  // extern "C"

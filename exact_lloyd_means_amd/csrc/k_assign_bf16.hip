@@ -1,0 +1,9 @@
+// k_assign_bf16.hip -- instantiations of the fused assign kernel for __bf16 inputs.
+#include "k_assign.inl"
+
+namespace fk {
+hipError_t launch_assign_bf16(const void* X, const void* C, const float* bias, int32_t* labels,
+                         float* min_dist, int64_t B, int64_t N, int64_t K, int d, hipStream_t s) {
+    return dispatch_assign<__bf16>(X, C, bias, labels, min_dist, B, N, K, d, s);
+}
+}  // namespace fk

@@ -1,0 +1,182 @@
+/*
+ * fk.h -- C ABI of an exact batched Lloyd k-means library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * One Lloyd iteration has two stages (7minutos.es article on Flash-KMeans,
+ * "¿Qué es Flash-KMeans?"; papernotes.org notes "Flash-KMeans: Fast and
+ * Memory-Efficient Exact K-Means", 方法详解 / 整体框架):
+ *   assign -- every point takes the index of its nearest centroid, found by a
+ *             fused distance + running (min, argmin) pass that never stores
+ *             the N x K distance matrix (papernotes.org notes, 关键设计 1);
+ *   update -- every centroid becomes the mean of its points, computed by
+ *             argsorting the labels and reducing contiguous same-label
+ *             segments, X never permuted (papernotes.org notes, 关键设计 2).
+ * The result equals textbook Lloyd; nothing is approximated.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Shapes   B independent problems with the same N (points), K (centroids)
+ *           and d (dimensions).  X is [B][N][d], C is [B][K][d], labels
+ *           [B][N], counts [B][K], offsets [B][K+1], all contiguous and
+ *           row-major.
+ *  Types    X and the centroids an assignment reads are stored in the
+ *           problem dtype (fp32, fp16 or bf16).  Dot products accumulate in
+ *           fp32.  Centroids carried between iterations, sums and the
+ *           centroid bias are fp32.  Labels, counts, offsets and sorted
+ *           indices are int32; labels are 0-based, in [0, K).
+ *  Ties     Among centroids at exactly equal computed distance the lowest
+ *           index wins.
+ *  Empty    A centroid with no points keeps its previous value bit for bit.
+ *  Memory   Every pointer is a device pointer unless marked "host".  Device
+ *           pointers must be 16-byte aligned.  The caller owns every buffer;
+ *           the library allocates no device memory, keeps no pointer after a
+ *           call returns and holds no state between calls (fk_last_error
+ *           aside).  Scratch space comes from the caller's workspace `ws`
+ *           of `ws_bytes` bytes (see fk_workspace_size).
+ *  Streams  `stream` is a hipStream_t passed as void*; NULL is the null
+ *           stream.  All device work is enqueued asynchronously on it.
+ *           Calls on different streams are safe when their workspaces and
+ *           outputs are distinct.
+ *  Errors   Arguments are checked on the host before anything is enqueued;
+ *           on an error nothing is enqueued and outputs are untouched.
+ *           FK_EINVAL     null required pointer, a size < 1, misalignment;
+ *           FK_EUNSUPPORTED unknown dtype or a size beyond the limits below;
+ *           FK_EWORKSPACE workspace missing or smaller than required;
+ *           FK_EHIP       a HIP runtime call or launch failed;
+ *           FK_EHOST      a host-side resource failed (streamed path).
+ *           fk_last_error() describes the most recent failure on the
+ *           calling thread.  Faults inside kernels surface at the caller's
+ *           next synchronisation.
+ *  Limits   N, K <= 2^31 - 2; d <= 65536.  Inputs must be finite, and
+ *           |c|^2 must be finite in fp32; otherwise labels are undefined.
+ */
+#ifndef FK_H
+#define FK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FK_ABI_VERSION 1
+
+typedef enum fk_dtype { FK_F32 = 0, FK_F16 = 1, FK_BF16 = 2 } fk_dtype;
+
+typedef enum fk_status {
+    FK_OK = 0,
+    FK_EINVAL = -1,
+    FK_EUNSUPPORTED = -2,
+    FK_EWORKSPACE = -3,
+    FK_EHIP = -4,
+    FK_EHOST = -5
+} fk_status;
+
+/* Problem description shared by all calls.  dtype is an fk_dtype value. */
+typedef struct fk_problem {
+    int64_t B, N, K, d;
+    int32_t dtype;
+    int32_t reserved; /* must be 0 */
+} fk_problem;
+
+/* Version of this ABI (FK_ABI_VERSION of the built library). */
+int fk_abi_version(void);
+
+/* Static text for a status code. */
+const char* fk_status_str(int status);
+
+/* Text of the most recent error on the calling thread ("" if none). */
+const char* fk_last_error(void);
+
+/*
+ * fk_workspace_size -- bytes of device workspace the other calls need for
+ * problem *p.  chunk_points = 0: fk_assign, fk_sort_labels, fk_update and
+ * fk_lloyd.  The size has no N x K term: the distance matrix is never stored
+ * (papernotes.org notes, 关键设计 1: IO falls from O(NK) to O(Nd + Kd)).
+ * *bytes (host) receives the size.
+ */
+fk_status fk_workspace_size(const fk_problem* p, int64_t chunk_points, size_t* bytes);
+
+/*
+ * fk_centroid_bias -- the centroid term of the distance expansion
+ * |x - c|^2 = |x|^2 + |c|^2 - 2 x.c (papernotes.org notes, 关键设计 1):
+ * bias[b][k] = -0.5 * sum_j C[b][k][j]^2, accumulated in fp32 from the
+ * stored dtype values of C [B][K][d].  bias is fp32 [B][K].
+ */
+fk_status fk_centroid_bias(const fk_problem* p, const void* C, float* bias, void* stream);
+
+/*
+ * fk_assign -- nearest centroid of every point (papernotes.org notes,
+ * 关键设计 1, running minimum m <- +inf, index a <- -1, merged by min/argmin).
+ * X [B][N][d] and C [B][K][d] in the problem dtype.  Writes labels [B][N]
+ * (int32, lowest index on exact ties of the fp32 score x.c - |c|^2/2) and,
+ * when min_dist is not NULL, min_dist [B][N] = |x|^2 - 2 max_k(x.c - |c|^2/2)
+ * in fp32, the squared distance to the chosen centroid.  Uses ws for the
+ * centroid bias.  The N x K distance matrix is never written.
+ */
+fk_status fk_assign(const fk_problem* p, const void* X, const void* C, int32_t* labels,
+                    float* min_dist, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * fk_sort_labels -- the argsort half of the update (papernotes.org notes,
+ * 关键设计 2: the 1-D label vector is argsorted so equal labels form
+ * contiguous segments).  From labels [B][N] writes
+ *   counts     [B][K]   number of points per label (exact);
+ *   offsets    [B][K+1] exclusive prefix sums of counts (offsets[b][K] = N);
+ *   sorted_idx [B][N]   point indices grouped by label: positions
+ *                       offsets[b][k] .. offsets[b][k+1]-1 hold the points of
+ *                       label k, in unspecified order within the segment.
+ * Labels outside [0, K) are skipped and counted (fk_error_count).
+ */
+fk_status fk_sort_labels(const fk_problem* p, const int32_t* labels, int32_t* counts,
+                         int32_t* offsets, int32_t* sorted_idx, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
+ * fk_update -- new centroids from labels (papernotes.org notes, 关键设计 2):
+ * argsort the labels, gather the rows of X of each contiguous same-label
+ * segment (X is not moved), sum them in fp32 with one atomic add per segment
+ * piece, then divide by the count.
+ *   X [B][N][d] problem dtype; labels [B][N];
+ *   C_prev [B][K][d] fp32, kept for empty clusters (may alias C_next);
+ *   C_next [B][K][d] fp32 = sum / count (IEEE fp32 division);
+ *   C_next_lowp [B][K][d] problem dtype = C_next rounded to nearest even,
+ *     may be NULL (must be NULL or distinct from C_next for fp32);
+ *   counts [B][K] int32.
+ * Centroid low bits depend on the order of fp32 atomic additions and can
+ * differ between runs; counts never do.
+ */
+fk_status fk_update(const fk_problem* p, const void* X, const int32_t* labels,
+                    const float* C_prev, float* C_next, void* C_next_lowp, int32_t* counts,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * fk_lloyd -- max_iters Lloyd iterations (papernotes.org notes, 整体框架
+ * flowchart: assign, update, repeat until converged or the iteration limit).
+ * C [B][K][d] fp32: initial centroids on entry, final ones on exit.  Each
+ * assignment reads C rounded to nearest even in the problem dtype.  labels
+ * [B][N] and counts [B][K] are those of the last assignment.  tol > 0 stops
+ * after the first iteration whose largest squared centroid move
+ * max_{b,k} |c_new - c_old|^2 is <= tol; tol == 0 runs exactly max_iters.
+ * n_iter (host, may be NULL) receives the number of iterations run.  With
+ * tol == 0 and n_iter == NULL nothing synchronises; otherwise the call
+ * synchronises the stream once per iteration.
+ */
+fk_status fk_lloyd(const fk_problem* p, const void* X, float* C, int32_t* labels,
+                   int32_t* counts, int max_iters, float tol, int* n_iter, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/*
+ * fk_error_count -- number of out-of-range labels skipped by the most recent
+ * fk_sort_labels / fk_update / fk_lloyd that used workspace ws.  Synchronises
+ * the stream.  *count is a host pointer.
+ */
+fk_status fk_error_count(const fk_problem* p, const void* ws, size_t ws_bytes, int64_t* count,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FK_H */

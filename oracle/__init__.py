@@ -54,6 +54,7 @@ def _bind(lib):
     lib.oracle_update.argtypes = [I, I, I64, I64, I64, I64, P, P, P, P, P, I]
     lib.oracle_update.restype = I64
     lib.oracle_lloyd.argtypes = [I, I64, I64, I64, I64, P, P, I64, P, P, P, I]
+    lib.oracle_pair_dist.argtypes = [I, I, I64, I64, I64, I64, P, P, P, P, I64, P]
     return lib
 
 
@@ -146,6 +147,23 @@ class Oracle:
                               _ptr(rows_arr), n, _ptr(labels), _ptr(d1), _ptr(d2), nthreads)
         return labels, d1, d2
 
+    def pair_dist(self, X: np.ndarray, C: np.ndarray, points: np.ndarray, cents: np.ndarray,
+                  fmt_x: str | None = None, fmt_c: str | None = None) -> np.ndarray:
+        """fp64 squared distance of each (flattened point id, centroid index) pair."""
+        B, N, d = X.shape
+        _, K, _ = C.shape
+        fx, fc = _dtype_name(X, fmt_x), _dtype_name(C, fmt_c)
+        Xs, Cs = _as_storage(X), _as_storage(C)
+        pts = np.ascontiguousarray(points, dtype=np.int64).reshape(-1)
+        cen = np.ascontiguousarray(cents, dtype=np.int32).reshape(-1)
+        assert pts.size == cen.size
+        assert pts.size == 0 or (pts.min() >= 0 and pts.max() < B * N)
+        assert cen.size == 0 or (cen.min() >= 0 and cen.max() < K)
+        out = np.empty(pts.size, dtype=np.float64)
+        self.lib.oracle_pair_dist(DTYPE_CODE[fx], DTYPE_CODE[fc], B, N, K, d, _ptr(Xs), _ptr(Cs),
+                                  _ptr(pts), _ptr(cen), pts.size, _ptr(out))
+        return out
+
     def update(self, X: np.ndarray, labels: np.ndarray, C_prev: np.ndarray, fmt_x: str | None = None,
                fmt_c: str | None = None, nthreads: int = 0):
         """Counts and per-cluster means from a given label vector.
@@ -230,6 +248,10 @@ def assign(*a, **k):
 
 def update(*a, **k):
     return default().update(*a, **k)
+
+
+def pair_dist(*a, **k):
+    return default().pair_dist(*a, **k)
 
 
 def lloyd(*a, **k):

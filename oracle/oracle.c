@@ -204,6 +204,31 @@ void oracle_assign(int dtype_x, int dtype_c, int64_t B, int64_t N, int64_t K, in
 }
 
 /* ---------------------------------------------------------------------------
+ * Squared distance of given (point, centroid) pairs, the same plain
+ * definition as in oracle_assign: sum_j (x_pj - c_kj)^2, fp64, j ascending.
+ * points[t] is a flattened point id b*N + i, cents[t] a centroid index of the
+ * same problem.  Used to check that a label chosen among near-ties is still
+ * near-optimal.
+ * ------------------------------------------------------------------------- */
+void oracle_pair_dist(int dtype_x, int dtype_c, int64_t B, int64_t N, int64_t K, int64_t d,
+                      const void* X, const void* C, const int64_t* points, const int32_t* cents,
+                      int64_t npairs, double* out) {
+    (void)B;
+    for (int64_t t = 0; t < npairs; ++t) {
+        const int64_t p = points[t];
+        const int64_t b = p / N;
+        const int64_t k = cents[t];
+        double dist = 0.0;
+        for (int64_t j = 0; j < d; ++j) {
+            const double diff = decode_one(dtype_x, X, p * d + j) -
+                                decode_one(dtype_c, C, (b * K + k) * d + j);
+            dist += diff * diff;
+        }
+        out[t] = dist;
+    }
+}
+
+/* ---------------------------------------------------------------------------
  * Update from a given label vector.
  *
  * counts[b,k] = number of i with labels[b,i] == k (exact integers).

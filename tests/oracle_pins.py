@@ -110,6 +110,13 @@ def pin_distance_expansion(orc):
     assert np.all(np.abs(d2 - Ds[..., 1]) <= bound * 2), "d2 is not the second minimum"
     chosen = np.take_along_axis(D, labels[..., None].astype(np.int64), -1)[..., 0]
     assert np.all(np.abs(chosen - d1) <= bound * 2), "label does not attain d1"
+    # sampled pair distances follow the same identity
+    rng2 = np.random.Generator(np.random.PCG64(12))
+    pts = rng2.integers(0, B * N, size=500)
+    cen = rng2.integers(0, K, size=500).astype(np.int32)
+    pd = orc.pair_dist(X, C, pts, cen)
+    ref = D.reshape(B * N, K)[pts, cen]
+    assert np.all(np.abs(pd - ref) <= 2 * bound.reshape(-1)[pts]), "pair distance differs"
     # small integers: every quantity is exact, so the identity holds exactly
     Xi, Ci = synth.integer_problem(2, 40, 7, 3, seed=3)
     Xi, Ci = Xi.astype(np.float64), Ci.astype(np.float64)

@@ -1,0 +1,140 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented status before
+touching the device (fake device addresses are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_lloyd_means_amd as fk
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "fk.h")
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced
+FAKE_MISALIGNED = 0x10004
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fk_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert "fk_assign" in names and "fk_update" in names and "fk_lloyd" in names
+    for name in names:
+        assert hasattr(fk.lib, name), f"{name} declared in fk.h but not exported"
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define FK_ABI_VERSION (\d+)", open(HEADER).read())
+    assert fk.abi_version() == int(m.group(1))
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert fk.lib.fk_status_str(code)
+    assert b"unknown" in fk.lib.fk_status_str(42)
+
+
+def P(B=2, N=100, K=10, d=16, dtype=fk.FK_F16, reserved=0):
+    return fk.Problem(B, N, K, d, dtype, reserved)
+
+
+def ws_size(p):
+    return fk.workspace_size(p)
+
+
+def call_assign(p, X=FAKE, C=FAKE, labels=FAKE, md=None, ws=FAKE, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = ws_size(p) if p.B > 0 and p.N > 0 and p.K > 0 and p.d > 0 else 0
+    return fk.lib.fk_assign(ctypes.byref(p) if p is not None else None, X, C, labels, md, ws,
+                            ws_bytes, None)
+
+
+@pytest.mark.parametrize("field", ["B", "N", "K", "d"])
+def test_sizes_below_one_rejected(field):
+    p = P()
+    setattr(p, field, 0)
+    assert call_assign(p) == fk.FK_EINVAL
+    assert b"sizes" in fk.lib.fk_last_error()
+
+
+def test_null_problem_rejected():
+    assert fk.lib.fk_assign(None, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == fk.FK_EINVAL
+
+
+def test_unknown_dtype_rejected():
+    assert call_assign(P(dtype=7), ws_bytes=1 << 30) == fk.FK_EUNSUPPORTED
+
+
+def test_reserved_must_be_zero():
+    assert call_assign(P(reserved=1), ws_bytes=1 << 30) == fk.FK_EINVAL
+
+
+@pytest.mark.parametrize("which", ["X", "C", "labels"])
+def test_null_and_misaligned_pointers(which):
+    p = P()
+    assert call_assign(p, **{which: None}) == fk.FK_EINVAL
+    assert call_assign(p, **{which: FAKE_MISALIGNED}) == fk.FK_EINVAL
+    assert b"aligned" in fk.lib.fk_last_error()
+
+
+def test_workspace_checks():
+    p = P()
+    assert call_assign(p, ws=None) == fk.FK_EWORKSPACE
+    assert call_assign(p, ws_bytes=ws_size(p) - 1) == fk.FK_EWORKSPACE
+    assert b"needs" in fk.lib.fk_last_error()
+
+
+def test_too_large_sizes():
+    assert call_assign(P(N=1 << 31), ws_bytes=0) == fk.FK_EUNSUPPORTED
+    assert call_assign(P(d=65537), ws_bytes=0) == fk.FK_EUNSUPPORTED
+
+
+def test_update_and_lloyd_validation():
+    p = P()
+    n = ws_size(p)
+    lib = fk.lib
+    # C_next missing
+    assert lib.fk_update(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, n,
+                         None) == fk.FK_EINVAL
+    # workspace too small
+    assert lib.fk_update(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, n - 256,
+                         None) == fk.FK_EWORKSPACE
+    # max_iters < 1, negative tol
+    assert lib.fk_lloyd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 0, 0.0, None, FAKE, n,
+                        None) == fk.FK_EINVAL
+    assert lib.fk_lloyd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 3, -1.0, None, FAKE, n,
+                        None) == fk.FK_EINVAL
+    # sort: offsets missing
+    assert lib.fk_sort_labels(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, n,
+                              None) == fk.FK_EINVAL
+    # error count: host pointer missing
+    assert lib.fk_error_count(ctypes.byref(p), FAKE, n, None, None) == fk.FK_EINVAL
+
+
+def test_workspace_has_no_NK_term():
+    """Workspace grows with B*N, B*K*d and B*K only (no distance matrix)."""
+    def size(B, N, K, d):
+        return fk.workspace_size(fk.problem(B, N, K, d, fk.FK_F16))
+    base = size(1, 1 << 16, 1 << 12, 128)
+    # doubling N adds one int32 per point (sorted indices), not K values per point
+    assert size(1, 1 << 17, 1 << 12, 128) - base <= 4 * (1 << 16) + 1024
+    # large N and K together stay far below N*K
+    big = size(1, 1 << 20, 1 << 16, 128)
+    assert big < (1 << 20) * (1 << 16) // 64
+    # config sizes
+    assert size(32, 65536, 1024, 128) < 64 << 20
+
+
+def test_last_error_is_per_call():
+    p = P()
+    call_assign(p, ws=None)
+    first = fk.lib.fk_last_error()
+    assert first
+    ok = fk.lib.fk_workspace_size(ctypes.byref(p), 0, ctypes.byref(ctypes.c_size_t()))
+    assert ok == fk.FK_OK

@@ -1,0 +1,119 @@
+"""Sort-inverse update (fk_sort_labels, fk_update) against the oracle on the GPU."""
+import numpy as np
+import pytest
+import torch
+
+import exact_lloyd_means_amd as fk
+import oracle
+from parity import TORCH, check_update
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+
+
+def sort_labels(labels, K):
+    B, N = labels.shape
+    counts = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    offsets = torch.empty((B, K + 1), dtype=torch.int32, device="cuda")
+    sidx = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    fk.fk_sort_labels(labels, K, counts, offsets, sidx)
+    torch.cuda.synchronize()
+    return counts.cpu().numpy(), offsets.cpu().numpy(), sidx.cpu().numpy()
+
+
+def check_sort(lab, K, counts, offsets, sidx):
+    B = lab.shape[0]
+    for b in range(B):
+        ref = np.bincount(lab[b], minlength=K)
+        assert np.array_equal(counts[b], ref)
+        assert offsets[b, 0] == 0 and np.array_equal(offsets[b, 1:], np.cumsum(ref))
+    assert oracle.argsort_valid(lab, sidx, K)
+
+
+@pytest.mark.parametrize("B,N,K", [(1, 1, 1), (3, 10000, 777), (2, 4097, 1024), (1, 5000, 9000),
+                                   (1, 70000, 65536), (2, 100, 16384), (1, 3000, 16385)])
+def test_sort_uniform(B, N, K):
+    g = torch.Generator().manual_seed(N + K)
+    lab = torch.randint(0, K, (B, N), generator=g, dtype=torch.int32)
+    c, o, s = sort_labels(lab.cuda(), K)
+    check_sort(lab.numpy(), K, c, o, s)
+
+
+def test_sort_skewed_and_constant():
+    g = torch.Generator().manual_seed(5)
+    K = 4096
+    j = torch.arange(1, K + 1, dtype=torch.float64)
+    p = j.pow(-1.2)
+    lab = torch.multinomial(p / p.sum(), 200000, replacement=True, generator=g).int().view(1, -1)
+    c, o, s = sort_labels(lab.cuda(), K)
+    check_sort(lab.numpy(), K, c, o, s)
+    lab0 = torch.zeros((2, 50000), dtype=torch.int32)
+    c, o, s = sort_labels(lab0.cuda(), 10)
+    check_sort(lab0.numpy(), 10, c, o, s)
+
+
+def run_update(X, labels, C_prev, want_lowp=True):
+    B, N, d = X.shape
+    K = C_prev.shape[1]
+    C_next = torch.empty_like(C_prev)
+    lowp = torch.empty((B, K, d), dtype=X.dtype, device="cuda") if (
+        want_lowp and X.dtype != torch.float32) else None
+    counts = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    fk.fk_update(X, labels, C_prev, C_next, lowp, counts)
+    torch.cuda.synchronize()
+    return C_next, lowp, counts
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("B,N,K,d", [(1, 1, 1, 1), (2, 5000, 100, 128), (1, 3000, 700, 3),
+                                     (3, 2000, 50, 129), (1, 1000, 20, 1024), (1, 4097, 64, 100),
+                                     (2, 100, 300, 64)])
+def test_update_vs_oracle(dt, B, N, K, d):
+    g = torch.Generator().manual_seed(B + N + K + d)
+    X = torch.randn((B, N, d), generator=g).to(TORCH[dt]).cuda()
+    # leave a few clusters empty
+    lab = torch.randint(0, max(1, K - 3), (B, N), generator=g, dtype=torch.int32).cuda()
+    C_prev = torch.randn((B, K, d), generator=g).cuda()
+    C_next, lowp, counts = run_update(X, lab, C_prev)
+    check_update(X, lab, C_prev, C_next, counts, lowp)
+
+
+def test_update_in_place_alias():
+    X = torch.randn((1, 3000, 64)).half().cuda()
+    lab = torch.randint(0, 40, (1, 3000), dtype=torch.int32).cuda()
+    C = torch.randn((1, 50, 64)).cuda()
+    C0 = C.clone()
+    counts = torch.empty((1, 50), dtype=torch.int32, device="cuda")
+    fk.fk_update(X, lab, C, C, None, counts)
+    torch.cuda.synchronize()
+    check_update(X, lab, C0, C, counts)
+
+
+def test_update_single_hot_cluster():
+    """Every point in one cluster: the whole sorted range is one segment."""
+    X = torch.randn((1, 200000, 128)).half().cuda()
+    lab = torch.zeros((1, 200000), dtype=torch.int32).cuda()
+    C_prev = torch.randn((1, 8, 128)).cuda()
+    C_next, lowp, counts = run_update(X, lab, C_prev)
+    check_update(X, lab, C_prev, C_next, counts, lowp)
+
+
+def test_update_out_of_range_labels_skipped():
+    B, N, K, d = 2, 3000, 30, 16
+    X = torch.randn((B, N, d)).cuda()
+    lab = torch.randint(0, K, (B, N), dtype=torch.int32)
+    lab[0, ::7] = -1
+    lab[1, ::11] = K
+    C_prev = torch.randn((B, K, d)).cuda()
+    p = fk.problem(B, N, K, d, torch.float32)
+    ws = fk.workspace(p)
+    C_next = torch.empty_like(C_prev)
+    counts = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    fk.fk_update(X, lab.cuda(), C_prev, C_next, None, counts, ws=ws)
+    n_bad = fk.fk_error_count(p, ws)
+    assert n_bad == int((lab < 0).sum() + (lab >= K).sum())
+    check_update(X, lab, C_prev, C_next, counts)

@@ -21,7 +21,8 @@ MUTANTS = {
     "centroids_of_problem_zero": ("const double* c = Cd + (b * K + k) * d;",
                                   "const double* c = Cd + k * d;"),
     "no_second_best": ("} else if (dist < second) {", "} else if (0) {"),
-    "abs_instead_of_square": ("dist += diff * diff;", "dist += fabs(diff);"),
+    "abs_instead_of_square": ("dist += diff * diff;\n                }\n                if (dist < best)",
+                              "dist += fabs(diff);\n                }\n                if (dist < best)"),
     # update: divisor, empty rule, batch index of labels
     "mean_divisor_off_by_one": ("sums[k * d + j] / (double)cnt[k]",
                                 "sums[k * d + j] / (double)(cnt[k] + 1)"),
