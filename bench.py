@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Lloyd iterations per second of the exact batched k-means path on one MI355X.
+
+One step = one Lloyd iteration over the whole batch: centroid bias, fused
+assign (MFMA), then the sort-inverse update (histogram, scan, scatter,
+segmented gather-sum, finalize), all in libfk's HIP kernels on the current
+torch stream.  Inputs are resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps 25] [--warmup 5] [--config 2]
+
+Prints one JSON line on stdout.  Stage times come from HIP events recorded
+on the stream the kernels run on.  The CPU baseline times the fp64 oracle on
+a bounded sample of the same workload and extrapolates linearly.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+# the pages' end-to-end time for this exact workload (H200, FP16): context only
+PAGES_MS_PER_ITER = {2: 6.2}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def assign_sources_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("k_assign.inl", "k_assign_f16.hip", "k_assign_bf16.hip", "k_assign_f32.hip"):
+        with open(os.path.join(ROOT, "exact_lloyd_means_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, src_hash: str):
+    """HBM bytes per assign launch from the committed PMC summary, if it was
+    taken on the current assign kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_assign_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("assign_sources_sha256_16") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=25)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..4 (see synth.CONFIGS)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run plain 1 GiB device copies (PMC byte-counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        msg = ("this build runs on one GPU only: pass --gpus 1 (the problems of a batch are "
+               "independent, so more GPUs would each take B/G problems; not built here)")
+        if int(os.environ.get("RANK", "0")) == 0:
+            log(msg)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import exact_lloyd_means_amd as fk
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = synth.CONFIGS[args.config]
+    fmt = w.dtype
+    log(f"[bench] generating {synth.describe(w)}")
+    t = time.time()
+    X_cpu, C0 = synth.make(w)
+    log(f"[bench] generated in {time.time() - t:.1f}s; uploading")
+    X = X_cpu.cuda()
+    B, N, d = X.shape
+    K = C0.shape[1]
+    C = C0.cuda()
+    Cq = C.to(X.dtype).contiguous() if fmt != "f32" else C
+    bias = torch.empty((B, K), dtype=torch.float32, device="cuda")
+    labels = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    counts = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    ws = fk.workspace(fk.problem(B, N, K, d, X.dtype))
+    lowp = Cq if fmt != "f32" else None
+
+    def step(e=None):
+        if e:
+            e[0].record()
+        fk.fk_centroid_bias(Cq, bias)
+        if e:
+            e[1].record()
+        fk.fk_assign_with_bias(X, Cq, bias, labels)
+        if e:
+            e[2].record()
+        # in place: C_prev and C_next alias; the RNE copy feeds the next assign
+        fk.fk_update(X, labels, C, C, lowp, counts, ws=ws)
+        if e:
+            e[3].record()
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = evs[0][0].elapsed_time(evs[-1][3])
+    bias_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    assign_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    update_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    log(f"[bench] {args.steps} steps: {total_ms:.3f} ms (events), {wall * 1e3:.3f} ms (wall)")
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    flops = 2.0 * B * N * K * d
+    xb = 4 if fmt == "f32" else 2
+    upd_bytes = B * N * d * xb + B * N * 4 + B * K * d * 4 + (B * K * d * xb if fmt != "f32" else 0) \
+        + B * K * 4
+    a_mean = float(np.mean(assign_ms))
+    u_mean = float(np.mean(update_ms))
+    achieved_tf = flops / (a_mean * 1e-3) / 1e12
+    peak_tf = PEAK_TFLOPS[fmt]
+    upd_gbs = upd_bytes / (u_mean * 1e-3) / 1e9
+    value = args.steps / (total_ms * 1e-3)
+    src_hash = assign_sources_hash()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = run_cpu_baseline(w, X_cpu, Cq, fmt, args.cpu_seconds, value)
+
+    pages_ms = PAGES_MS_PER_ITER.get(args.config)
+    out = {
+        "metric": "Lloyd iters/sec at B=32,N=65536,K=1024,d=128 fp16; assign MFMA %, update HBM %"
+        if args.config == 2 else f"Lloyd iters/sec at {synth.describe(w)}",
+        "value": round(value, 3),
+        "unit": "Lloyd it/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / (1000.0 / pages_ms), 3) if pages_ms else None,
+        "dtype": fmt,
+        "data": "synthetic: seeded Gaussian mixture in HBM (" + synth.describe(w) + ")",
+        "config": {"workload": w.name, "B": B, "N": N, "K": K, "d": d, "dtype": fmt,
+                   "step": "1 Lloyd iteration (bias + fused assign + sort-inverse update)"},
+        "stages": {
+            "bias_ms": round(float(np.mean(bias_ms)), 4),
+            "assign_ms": round(a_mean, 4),
+            "update_ms": round(u_mean, 4),
+            "assign_mfma_frac": round(achieved_tf / peak_tf, 4),
+            "update_hbm_frac": round(upd_gbs / PEAK_HBM_GBS, 4),
+            "update_algorithmic_bytes": upd_bytes,
+            "update_GBps": round(upd_gbs, 1),
+            "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        },
+        "roofline": {
+            "kernel": "k_assign (fused distance + argmin)",
+            "bound": "mfma",
+            "achieved": round(achieved_tf, 2),
+            "peak": peak_tf,
+            "unit": "TFLOP/s",
+            "frac": round(achieved_tf / peak_tf, 4),
+            "traffic": measured_traffic(w.name, src_hash),
+            "algorithmic_flops_per_launch": flops,
+            "assign_sources_sha256_16": src_hash,
+        },
+        "cpu_baseline": cpu,
+    }
+    if pages_ms:
+        out["baseline_context"] = f"pages: {pages_ms} ms/iter on NVIDIA H200 (FP16), not this machine"
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def run_cpu_baseline(w, X_cpu, Cq, fmt, target_s, gpu_value):
+    import numpy as np
+    import torch
+
+    import oracle
+
+    def storage(t):
+        t = t.detach().contiguous().cpu()
+        if t.dtype == torch.float32:
+            return t.numpy()
+        return t.view(torch.int16).numpy().view(np.uint16)
+
+    Xs, Cs = storage(X_cpu), storage(Cq)
+    B, N, d = Xs.shape
+    total = B * N
+    rng = np.random.Generator(np.random.PCG64(7))
+    threads = oracle.max_threads()
+    # probe, then size the sample for about target_s of assign work
+    probe = rng.choice(total, size=min(total, 256), replace=False)
+    t = time.perf_counter()
+    oracle.assign(Xs, Cs, fmt_x=fmt, fmt_c=fmt, rows=probe)
+    per_row = (time.perf_counter() - t) / probe.size
+    S = int(min(total, max(256, target_s / max(per_row, 1e-9))))
+    rows = rng.choice(total, size=S, replace=False)
+    log(f"[bench] cpu baseline: oracle assign on {S} of {total} points, {threads} threads")
+    t = time.perf_counter()
+    lab, _, _ = oracle.assign(Xs, Cs, fmt_x=fmt, fmt_c=fmt, rows=rows)
+    t_assign = (time.perf_counter() - t) * total / S
+    # update of one whole problem, scaled by B
+    lab0 = np.zeros((1, N), np.int32)
+    lab0[0, :] = np.arange(N) % Cs.shape[1]
+    t = time.perf_counter()
+    oracle.update(Xs[:1], lab0, np.zeros((1, Cs.shape[1], d), np.float32), fmt_x=fmt, fmt_c="f32")
+    t_update = (time.perf_counter() - t) * B
+    it_s = 1.0 / (t_assign + t_update)
+    return {
+        "value": it_s,
+        "unit": "Lloyd it/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fp64 oracle assign on {S} random points of {total} (x{total / S:.1f} "
+                   f"extrapolated, linear in points) + update of 1 of {B} problems (x{B}); "
+                   f"{t_assign:.1f} s assign + {t_update:.2f} s update per iteration"),
+        "gpu_over_cpu": round(gpu_value / it_s, 1),
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())

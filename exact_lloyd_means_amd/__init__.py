@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libfk.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m exact_lloyd_means_amd.build` "
+        f"{LIB_PATH} is not built; run `python exact_lloyd_means_amd/build.py` "
         "(or __graft_entry__.build()) first")
 
 lib = ctypes.CDLL(LIB_PATH)
@@ -44,6 +44,7 @@ _SIG = {
     "fk_workspace_size": ([_PP, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "fk_centroid_bias": ([_PP, _P, _P, _P], ctypes.c_int),
     "fk_assign": ([_PP, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "fk_assign_with_bias": ([_PP, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "fk_sort_labels": ([_PP, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "fk_update": ([_PP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "fk_lloyd": ([_PP, _P, _P, _P, _P, ctypes.c_int, ctypes.c_float,
@@ -131,6 +132,16 @@ def fk_assign(X: torch.Tensor, C: torch.Tensor, labels: torch.Tensor,
     ws = workspace(p, X.device) if ws is None else ws
     _check(lib.fk_assign(ctypes.byref(p), _ptr(X), _ptr(C), _ptr(labels), _ptr(min_dist),
                          _ptr(ws), ws.numel(), _stream(stream)), "fk_assign")
+
+
+def fk_assign_with_bias(X: torch.Tensor, C: torch.Tensor, bias: torch.Tensor,
+                        labels: torch.Tensor, min_dist: torch.Tensor | None = None,
+                        stream=None) -> None:
+    p = _problem_from(X, C.shape[1])
+    if C.dtype != X.dtype:
+        raise ValueError("C must have the dtype of X")
+    _check(lib.fk_assign_with_bias(ctypes.byref(p), _ptr(X), _ptr(C), _ptr(bias), _ptr(labels),
+                                   _ptr(min_dist), _stream(stream)), "fk_assign_with_bias")
 
 
 def fk_sort_labels(labels: torch.Tensor, K: int, counts: torch.Tensor, offsets: torch.Tensor,

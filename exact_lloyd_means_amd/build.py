@@ -1,6 +1,9 @@
 """Builds libfk.so (in-tree, next to this file) with hipcc for gfx950.
 
-    python -m exact_lloyd_means_amd.build
+    python exact_lloyd_means_amd/build.py
+
+Run it as a script (not as a package module): the package's __init__ loads
+the built library, which may be missing or stale before a build.
 
 Each translation unit compiles to an object under _build/, then hipcc links
 the shared library.  Every call rebuilds everything.
@@ -24,6 +27,7 @@ SOURCES = ["fk_api.hip", "k_update.hip", "k_assign_f16.hip", "k_assign_bf16.hip"
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-munsafe-fp-atomics",                      # hardware fp32 atomic add
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",       # MFMA accumulators in VGPRs (no AGPR copies)
     # packed fp32 instructions are kept out of generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",

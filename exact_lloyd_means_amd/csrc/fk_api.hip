@@ -191,6 +191,21 @@ fk_status fk_assign(const fk_problem* p, const void* X, const void* C, int32_t* 
     return FK_OK;
 }
 
+fk_status fk_assign_with_bias(const fk_problem* p, const void* X, const void* C,
+                              const float* bias, int32_t* labels, float* min_dist, void* stream) {
+    FK_CHECK(check_problem(p));
+    FK_CHECK(check_ptr(X, "X"));
+    FK_CHECK(check_ptr(C, "C"));
+    FK_CHECK(check_ptr(bias, "bias"));
+    FK_CHECK(check_ptr(labels, "labels"));
+    FK_CHECK(check_ptr(min_dist, "min_dist", false));
+    FK_CHECK(check_assign_d(*p));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    FK_TRY(launch_assign(p->dtype, X, C, bias, labels, min_dist, p->B, p->N, p->K, (int)p->d, s),
+           "assign");
+    return FK_OK;
+}
+
 fk_status fk_sort_labels(const fk_problem* p, const int32_t* labels, int32_t* counts,
                          int32_t* offsets, int32_t* sorted_idx, void* ws, size_t ws_bytes,
                          void* stream) {

@@ -117,19 +117,29 @@ __device__ inline u32x4 load_chunk(const T* __restrict__ base, int64_t row, int6
 }
 
 // Q  = 16-byte chunks per half row (HR = Q * 16 / sizeof(T) dimensions),
-// NB = 32-point column blocks held by each wave.
-template <typename T, int Q, int NB, bool VEC>
-__global__ __launch_bounds__(kAssignWaves * kWave) void k_assign(
-    const T* __restrict__ X, const T* __restrict__ C, const float* __restrict__ bias,
-    int32_t* __restrict__ labels, float* __restrict__ min_dist, int64_t N, int64_t K, int d) {
+// NB = 32-point column blocks held by each wave,
+// VEC   = d is a multiple of the 16-byte chunk (rows load as whole chunks),
+// EXACT = d equals the padded row length 2*HR (no column checks at all).
+//
+// Pipeline per wave: the MFMAs of tile t+1 are issued before the compare /
+// select epilogue of tile t, so matrix and vector units work at the same
+// time; the global loads of tile t+2 are in flight meanwhile and land in the
+// LDS buffer tile t used.  One barrier per tile.
+template <typename T, int Q, int NB, bool VEC, bool EXACT>
+__global__ __launch_bounds__(kAssignWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __restrict__ bias,
+              int32_t* __restrict__ labels, float* __restrict__ min_dist, int64_t N, int64_t K,
+              int d) {
     using M = Mfma<T>;
     constexpr int V = 16 / sizeof(T);
     constexpr int HR = Q * V;                          // dimensions per half row
     constexpr int ROWB = 2 * Q * 16 + 16;              // LDS bytes per centroid row (padded)
     constexpr int TILEB = kAssignBK * ROWB;
     constexpr int CHUNKS = kAssignBK * 2 * Q;          // 16-byte chunks per tile
-    constexpr int PER = (CHUNKS + kAssignWaves * kWave - 1) / (kAssignWaves * kWave);
+    constexpr int NT = kAssignWaves * kWave;
+    constexpr int PER = (CHUNKS + NT - 1) / NT;
     constexpr int PTS = kAssignWaves * NB * 32;        // points per workgroup
+    static_assert(!EXACT || VEC, "EXACT implies VEC");
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* s_tile = smem;                                            // [2][TILEB]
@@ -145,6 +155,7 @@ __global__ __launch_bounds__(kAssignWaves * kWave) void k_assign(
     const T* __restrict__ Cb = C + b * K * d;
     const float* __restrict__ biasb = bias + b * K;
     const int64_t pbase = (int64_t)blockIdx.x * PTS + (int64_t)wave * NB * 32;
+    const int ntiles = (int)((K + kAssignBK - 1) / kAssignBK);
 
     // ---- points of this wave: resident for the whole K loop
     u32x4 xf[NB][Q];
@@ -154,57 +165,65 @@ __global__ __launch_bounds__(kAssignWaves * kWave) void k_assign(
         xsq[nb] = 0.f;
         const int64_t j = pbase + nb * 32 + col;
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            xf[nb][q] = load_chunk<T, VEC>(Xb, j, N, d, h * HR + q * V);
-            if (min_dist) xsq[nb] += M::sumsq(xf[nb][q]);
-        }
+        for (int q = 0; q < Q; ++q) xf[nb][q] = load_chunk<T, VEC>(Xb, j, N, d, h * HR + q * V);
+    }
+    if (min_dist) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int q = 0; q < Q; ++q) xsq[nb] += M::sumsq(xf[nb][q]);
     }
 
-    // ---- centroid tile staging (registers -> LDS)
-    u32x4 pre[PER];
-    float pre_bias = 0.f;
-    auto gload = [&](int64_t tbase) {
+    // ---- centroid tile staging (registers -> LDS).  Thread tid always moves
+    // the same (row, chunk) pairs of a tile.  Rows past K (last tile only)
+    // re-read row K-1: any finite data will do, their bias is -inf.  Chunks
+    // past d re-read the row's last chunk: the X side of those dimensions is
+    // zero, so they add nothing.
+    int crow[PER], ccol[PER], cofs[PER];
+    const int K32 = (int)K;
 #pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int c = tid + u * kAssignWaves * kWave;
-            if (c < CHUNKS) {
-                const int r = c / (2 * Q);
-                const int cc = c % (2 * Q);
-                pre[u] = load_chunk<T, VEC>(Cb, tbase + r, K, d, cc * V);
-            }
-        }
-        if (tid < kAssignBK) pre_bias = (tbase + tid < K) ? biasb[tbase + tid] : -INFINITY;
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int c = tid + u * kAssignWaves * kWave;
-            if (c < CHUNKS) {
-                const int r = c / (2 * Q);
-                const int cc = c % (2 * Q);
-                *reinterpret_cast<u32x4*>(s_tile + buf * TILEB + r * ROWB + cc * 16) = pre[u];
-            }
-        }
-        if (tid < kAssignBK) s_bias[buf * kAssignBK + tid] = pre_bias;
-    };
-
-    float best[NB];
-    int32_t bidx[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        best[nb] = -INFINITY;
-        bidx[nb] = 0;
+    for (int u = 0; u < PER; ++u) {
+        const int c = tid + u * NT;
+        crow[u] = c / (2 * Q);
+        ccol[u] = c % (2 * Q);
+        cofs[u] = EXACT ? ccol[u] * V : min(ccol[u] * V, d - V);
     }
+    struct Staged {
+        u32x4 v[PER];
+        float bias;
+    };
+    // Branch-free so the compiler can keep several tiles of loads in flight:
+    // loads are issued for every t (rows clamped, so a t past the last tile
+    // just re-reads row K-1) and every thread fetches one bias value.
+    auto gload = [&](int t, Staged& st) {
+        const int tbase = t * kAssignBK;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            if (CHUNKS % NT == 0 || u * NT + tid < CHUNKS) {
+                if constexpr (VEC) {
+                    const int row = min(tbase + crow[u], K32 - 1);
+                    st.v[u] = *reinterpret_cast<const u32x4*>(Cb + (int64_t)row * d + cofs[u]);
+                } else {
+                    st.v[u] = load_chunk<T, false>(Cb, tbase + crow[u], K, d, ccol[u] * V);
+                }
+            }
+        }
+        const int k = tbase + (tid & (kAssignBK - 1));
+        const float v = biasb[min(k, K32 - 1)];
+        st.bias = k < K32 ? v : -INFINITY;
+    };
+    auto sstore = [&](int buf, const Staged& st) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u)
+            if (CHUNKS % NT == 0 || u * NT + tid < CHUNKS)
+                *reinterpret_cast<u32x4*>(s_tile + buf * TILEB + crow[u] * ROWB + ccol[u] * 16) =
+                    st.v[u];
+        if (tid < kAssignBK) s_bias[buf * kAssignBK + tid] = st.bias;
+    };
 
-    const int64_t ntiles = (K + kAssignBK - 1) / kAssignBK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int64_t t = 0; t < ntiles; ++t) {
-        const int buf = (int)(t & 1);
-        if (t + 1 < ntiles) gload((t + 1) * kAssignBK);
-
-        // bias of rows 8g + 4h + i (g = 0..3, i = 0..3): the accumulator rows of this lane
+    // MFMAs of the tile in LDS buffer `buf`; the accumulators start at the
+    // bias of their rows (8g + 4h + i, g, i = 0..3).
+    auto mma = [&](int buf, floatx16 (&acc)[NB]) {
         floatx16 bv;
         const float* sb = s_bias + buf * kAssignBK + 4 * h;
 #pragma unroll
@@ -215,8 +234,6 @@ __global__ __launch_bounds__(kAssignWaves * kWave) void k_assign(
             bv[4 * g + 2] = v4[2];
             bv[4 * g + 3] = v4[3];
         }
-
-        floatx16 acc[NB];
         const char* arow = s_tile + buf * TILEB + col * ROWB + h * Q * 16;
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
@@ -228,22 +245,77 @@ __global__ __launch_bounds__(kAssignWaves * kWave) void k_assign(
                     acc[nb] = M::step(a, xf[nb][q], (q == 0 && e == 0) ? bv : acc[nb], e);
             }
         }
+    };
 
-        // epilogue: running (max score, lowest index); rows ascend with r
-        const int32_t kb = (int32_t)(t * kAssignBK);
+    float best[NB];
+    int32_t bidx[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        best[nb] = -INFINITY;
+        bidx[nb] = 0;
+    }
+    // Running (max score, lowest index).  Within a tile the candidate index is
+    // the lane's row offset 8*(r/4) + r%4 (a small inline constant, -1 = no
+    // improvement in this tile); rows ascend with r, so strict > keeps the
+    // lowest index.  The tile base is added once per tile.
+    auto epilogue = [&](const floatx16 (&acc)[NB], int t) {
+        const int32_t kb = t * kAssignBK;
+        float m[NB];
+        int32_t rt[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
+            m[nb] = best[nb];
+            rt[nb] = -1;
+        }
+        // the NB chains are independent; interleaving them spaces each
+        // compare from the select that consumes it
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < 16; ++r) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
                 const float s = acc[nb][r];
-                const bool better = s > best[nb];
-                best[nb] = better ? s : best[nb];
-                bidx[nb] = better ? kb + 8 * (r >> 2) + (r & 3) : bidx[nb];
+                // written as "keep" so both selects take the 2-operand form
+                const bool keep = !(s > m[nb]);
+                m[nb] = keep ? m[nb] : s;
+                rt[nb] = keep ? rt[nb] : 8 * (r >> 2) + (r & 3);
             }
         }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            best[nb] = m[nb];
+            bidx[nb] = rt[nb] >= 0 ? kb + rt[nb] : bidx[nb];
+        }
+    };
 
-        if (t + 1 < ntiles) sstore(buf ^ 1);
+    // Prefetch distance: the loads of tile t+3 are issued in iteration t and
+    // reach LDS in iteration t+1, so a global load has more than a full
+    // iteration to land.
+    floatx16 acc0[NB], acc1[NB];
+    Staged st0, st1;
+    gload(0, st0);
+    gload(1, st1);
+    sstore(0, st0);
+    __syncthreads();
+    mma(0, acc0);
+    sstore(1, st1);
+    gload(2, st0);
+    __syncthreads();
+
+    // iteration t: tile t's scores are in accA, tile t+1 is in LDS buffer
+    // (t+1)&1, tile t+2 is in flight in stA, stB is free.  Loads and stores
+    // run unconditionally (past the last tile they move unused data).
+    auto iteration = [&](int t, floatx16 (&accA)[NB], floatx16 (&accB)[NB], Staged& stA,
+                         Staged& stB) {
+        gload(t + 3, stB);
+        if (t + 1 < ntiles) mma((t + 1) & 1, accB);
+        epilogue(accA, t);
+        sstore(t & 1, stA);
         __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        iteration(t, acc0, acc1, st0, st1);
+        if (t + 1 >= ntiles) break;
+        iteration(t + 1, acc1, acc0, st1, st0);
     }
 
     // ---- merge the two half-waves that hold the same point; write the label
@@ -266,14 +338,14 @@ __global__ __launch_bounds__(kAssignWaves * kWave) void k_assign(
     }
 }
 
-template <typename T, int Q, int NB, bool VEC>
+template <typename T, int Q, int NB, bool VEC, bool EXACT>
 hipError_t launch_assign_t(const void* X, const void* C, const float* bias, int32_t* labels,
                            float* min_dist, int64_t B, int64_t N, int64_t K, int d,
                            hipStream_t s) {
     constexpr int ROWB = 2 * Q * 16 + 16;
     constexpr size_t lds = 2 * (size_t)kAssignBK * ROWB + 2 * kAssignBK * sizeof(float);
     constexpr int PTS = kAssignWaves * NB * 32;
-    auto kern = k_assign<T, Q, NB, VEC>;
+    auto kern = k_assign<T, Q, NB, VEC, EXACT>;
     static bool attr_set = false;  // one attribute call per instantiation and process
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -297,17 +369,22 @@ hipError_t dispatch_assign(const void* X, const void* C, const float* bias, int3
     constexpr int V = 16 / sizeof(T);
     const int need = (d + 2 * V - 1) / (2 * V);  // chunks per half row
     const bool vec = (d % V) == 0;
-#define FK_ASSIGN_CASE(QQ, NBB)                                                               \
-    if (need <= QQ)                                                                           \
-        return vec ? launch_assign_t<T, QQ, NBB, true>(X, C, bias, labels, min_dist, B, N, K, \
-                                                       d, s)                                  \
-                   : launch_assign_t<T, QQ, NBB, false>(X, C, bias, labels, min_dist, B, N,   \
-                                                        K, d, s);
-    FK_ASSIGN_CASE(1, 4)
-    FK_ASSIGN_CASE(2, 4)
-    FK_ASSIGN_CASE(4, 4)
-    FK_ASSIGN_CASE(8, 4)
-    FK_ASSIGN_CASE(16, 2)
+#define FK_ASSIGN_CASE(QQ, NBB)                                                              \
+    if (need <= QQ) {                                                                        \
+        if (vec && d == 2 * QQ * V)                                                          \
+            return launch_assign_t<T, QQ, NBB, true, true>(X, C, bias, labels, min_dist, B, N, \
+                                                           K, d, s);                         \
+        if (vec)                                                                             \
+            return launch_assign_t<T, QQ, NBB, true, false>(X, C, bias, labels, min_dist, B,   \
+                                                            N, K, d, s);                     \
+        return launch_assign_t<T, QQ, NBB, false, false>(X, C, bias, labels, min_dist, B, N,   \
+                                                         K, d, s);                           \
+    }
+    FK_ASSIGN_CASE(1, 2)
+    FK_ASSIGN_CASE(2, 2)
+    FK_ASSIGN_CASE(4, 2)
+    FK_ASSIGN_CASE(8, 2)
+    FK_ASSIGN_CASE(16, 1)
     FK_ASSIGN_CASE(32, 1)
 #undef FK_ASSIGN_CASE
     return hipErrorInvalidValue;

@@ -119,6 +119,16 @@ fk_status fk_assign(const fk_problem* p, const void* X, const void* C, int32_t* 
                     float* min_dist, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * fk_assign_with_bias -- fk_assign with the centroid bias supplied by the
+ * caller: bias [B][K] fp32 must equal fk_centroid_bias(C) for the result to
+ * be the nearest-centroid assignment.  Needs no workspace.  Lets a caller
+ * that keeps C fixed over many assignments (or that gets the bias from
+ * fk_lloyd's finalize) skip the bias pass.
+ */
+fk_status fk_assign_with_bias(const fk_problem* p, const void* X, const void* C,
+                              const float* bias, int32_t* labels, float* min_dist, void* stream);
+
+/*
  * fk_sort_labels -- the argsort half of the update (papernotes.org notes,
  * 关键设计 2: the 1-D label vector is argsorted so equal labels form
  * contiguous segments).  From labels [B][N] writes

@@ -123,3 +123,22 @@ def test_misaligned_view_rejected():
     labels = torch.empty((1, 64), dtype=torch.int32, device="cuda")
     with pytest.raises(fk.FKError):
         fk.fk_assign(Xv, C, labels)
+
+
+@pytest.mark.parametrize("dt", DT)
+def test_assign_with_bias_matches_assign(dt):
+    X, C0 = synth.make(2, B=2, N=3000, K=300, dtype=dt)
+    X = X.cuda()
+    C = C0.to(X.dtype).cuda()
+    a, ma = run_assign(X, C)
+    bias = torch.empty((2, 300), dtype=torch.float32, device="cuda")
+    fk.fk_centroid_bias(C, bias)
+    lab = torch.empty_like(a)
+    md = torch.empty_like(ma)
+    fk.fk_assign_with_bias(X, C, bias, lab, md)
+    torch.cuda.synchronize()
+    assert torch.equal(a, lab) and torch.equal(ma, md)
+    # the bias is -|c|^2/2 of the stored values
+    cc = oracle.decode(to_storage(C), dt).astype(np.float64)
+    ref = -0.5 * (cc ** 2).sum(-1)
+    assert np.allclose(bias.cpu().numpy(), ref, rtol=1e-6, atol=1e-6)
