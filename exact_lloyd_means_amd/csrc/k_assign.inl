@@ -119,13 +119,17 @@ __device__ inline u32x4 load_chunk(const T* __restrict__ base, int64_t row, int6
 // Q  = 16-byte chunks per half row (HR = Q * 16 / sizeof(T) dimensions),
 // NB = 32-point column blocks held by each wave,
 // VEC   = d is a multiple of the 16-byte chunk (rows load as whole chunks),
-// EXACT = d equals the padded row length 2*HR (no column checks at all).
+// EXACT = d equals the padded row length 2*HR (no column checks at all),
+// SMALLK = K < 32: the single tile is padded with -inf-bias rows.  For
+//   K >= 32 the last tile instead starts at K-32 and overlaps the previous
+//   one; seeing a centroid twice cannot change a strict-">" running argmax
+//   (same score, later in the scan), so no padding is needed.
 //
 // Pipeline per wave: the MFMAs of tile t+1 are issued before the compare /
 // select epilogue of tile t, so matrix and vector units work at the same
 // time; the global loads of tile t+2 are in flight meanwhile and land in the
 // LDS buffer tile t used.  One barrier per tile.
-template <typename T, int Q, int NB, bool VEC, bool EXACT>
+template <typename T, int Q, int NB, bool VEC, bool EXACT, bool SMALLK>
 __global__ __launch_bounds__(kAssignWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __restrict__ bias,
               int32_t* __restrict__ labels, float* __restrict__ min_dist, int64_t N, int64_t K,
@@ -175,42 +179,48 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
     }
 
     // ---- centroid tile staging (registers -> LDS).  Thread tid always moves
-    // the same (row, chunk) pairs of a tile.  Rows past K (last tile only)
-    // re-read row K-1: any finite data will do, their bias is -inf.  Chunks
-    // past d re-read the row's last chunk: the X side of those dimensions is
-    // zero, so they add nothing.
-    int crow[PER], ccol[PER], cofs[PER];
+    // the same (row, chunk) pairs of a tile, so each load is a uniform tile
+    // base plus a loop-invariant per-thread offset.  Chunks past d re-read
+    // the row's last chunk: the X side of those dimensions is zero, so they
+    // add nothing.  Loads are issued for every t (a t past the last tile
+    // re-reads the last tile) so the loop has no branches around them.
+    int crow[PER], ccol[PER];
+    uint32_t goff[PER];
     const int K32 = (int)K;
+    const int lastbase = SMALLK ? 0 : K32 - kAssignBK;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
         const int c = tid + u * NT;
         crow[u] = c / (2 * Q);
         ccol[u] = c % (2 * Q);
-        cofs[u] = EXACT ? ccol[u] * V : min(ccol[u] * V, d - V);
+        const int cofs = EXACT ? ccol[u] * V : min(ccol[u] * V, d - V);
+        goff[u] = (uint32_t)((crow[u] * d + cofs) * (int)sizeof(T));
     }
+    auto tile_base = [&](int t) { return SMALLK ? 0 : min(t * kAssignBK, lastbase); };
     struct Staged {
         u32x4 v[PER];
         float bias;
     };
-    // Branch-free so the compiler can keep several tiles of loads in flight:
-    // loads are issued for every t (rows clamped, so a t past the last tile
-    // just re-reads row K-1) and every thread fetches one bias value.
     auto gload = [&](int t, Staged& st) {
-        const int tbase = t * kAssignBK;
+        const int tbase = tile_base(t);
+        const char* base = reinterpret_cast<const char*>(Cb + (int64_t)tbase * d);
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
             if (CHUNKS % NT == 0 || u * NT + tid < CHUNKS) {
-                if constexpr (VEC) {
-                    const int row = min(tbase + crow[u], K32 - 1);
-                    st.v[u] = *reinterpret_cast<const u32x4*>(Cb + (int64_t)row * d + cofs[u]);
+                if constexpr (SMALLK || !VEC) {
+                    st.v[u] = load_chunk<T, VEC>(Cb, tbase + crow[u], K, d, ccol[u] * V);
                 } else {
-                    st.v[u] = load_chunk<T, false>(Cb, tbase + crow[u], K, d, ccol[u] * V);
+                    st.v[u] = *reinterpret_cast<const u32x4*>(base + goff[u]);
                 }
             }
         }
-        const int k = tbase + (tid & (kAssignBK - 1));
-        const float v = biasb[min(k, K32 - 1)];
-        st.bias = k < K32 ? v : -INFINITY;
+        if constexpr (SMALLK) {
+            const int k = tid & (kAssignBK - 1);
+            const float v = biasb[min(k, K32 - 1)];
+            st.bias = k < K32 ? v : -INFINITY;
+        } else {
+            st.bias = biasb[tbase + (tid & (kAssignBK - 1))];
+        }
     };
     auto sstore = [&](int buf, const Staged& st) {
 #pragma unroll
@@ -218,7 +228,9 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
             if (CHUNKS % NT == 0 || u * NT + tid < CHUNKS)
                 *reinterpret_cast<u32x4*>(s_tile + buf * TILEB + crow[u] * ROWB + ccol[u] * 16) =
                     st.v[u];
-        if (tid < kAssignBK) s_bias[buf * kAssignBK + tid] = st.bias;
+        // every thread stores its bias value (8 identical stores per slot), so
+        // the loop body has no branch
+        s_bias[buf * kAssignBK + (tid & (kAssignBK - 1))] = st.bias;
     };
 
     // MFMAs of the tile in LDS buffer `buf`; the accumulators start at the
@@ -259,7 +271,7 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
     // improvement in this tile); rows ascend with r, so strict > keeps the
     // lowest index.  The tile base is added once per tile.
     auto epilogue = [&](const floatx16 (&acc)[NB], int t) {
-        const int32_t kb = t * kAssignBK;
+        const int32_t kb = tile_base(t);
         float m[NB];
         int32_t rt[NB];
 #pragma unroll
@@ -291,31 +303,68 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
     // reach LDS in iteration t+1, so a global load has more than a full
     // iteration to land.
     floatx16 acc0[NB], acc1[NB];
-    Staged st0, st1;
+    // Four staging register sets: the loads of tile t+4 are issued in
+    // iteration t and reach LDS in iteration t+2, two iterations later.
+    Staged st0, st1, st2, st3;
     gload(0, st0);
     gload(1, st1);
+    gload(2, st2);
+    gload(3, st3);
     sstore(0, st0);
     __syncthreads();
     mma(0, acc0);
     sstore(1, st1);
-    gload(2, st0);
     __syncthreads();
 
-    // iteration t: tile t's scores are in accA, tile t+1 is in LDS buffer
-    // (t+1)&1, tile t+2 is in flight in stA, stB is free.  Loads and stores
-    // run unconditionally (past the last tile they move unused data).
-    auto iteration = [&](int t, floatx16 (&accA)[NB], floatx16 (&accB)[NB], Staged& stA,
-                         Staged& stB) {
-        gload(t + 3, stB);
-        if (t + 1 < ntiles) mma((t + 1) & 1, accB);
+    // iteration t (t + 1 < ntiles): tile t's scores are in accA, tile t+1 is
+    // in LDS buffer (t+1)&1, tile t+2 waits in stS (loaded two iterations
+    // ago) and stL receives tile t+4.
+    // The body is one basic block; the schedule below interleaves every MFMA
+    // of tile t+1 with about six epilogue instructions of tile t, so the
+    // vector unit works while the matrix unit runs.  Loads and stores past
+    // the last tile move unused data.
+    auto iteration = [&](int t, floatx16 (&accA)[NB], floatx16 (&accB)[NB], Staged& stS,
+                         Staged& stL) {
+        gload(t + 4, stL);
+        mma((t + 1) & 1, accB);
         epilogue(accA, t);
-        sstore(t & 1, stA);
+        sstore(t & 1, stS);
+        constexpr int kMfma = NB * Q * M::kSteps;
+        constexpr int kValuPer = (NB * 48 + kMfma - 1) / kMfma + 1;
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // bias + first A fragment reads
+        __builtin_amdgcn_sched_group_barrier(0x020, PER + 1, 0);  // global loads, tile t+4
+#pragma unroll
+        for (int i = 0; i < kMfma; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);  // epilogue VALU
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // next A fragment read
+        }
         __syncthreads();
     };
-    for (int t = 0; t < ntiles; t += 2) {
-        iteration(t, acc0, acc1, st0, st1);
-        if (t + 1 >= ntiles) break;
-        iteration(t + 1, acc1, acc0, st1, st0);
+    // set holding tile j: st[j % 4]; iteration t stores tile t+2 and loads t+4
+    int t = 0;
+    for (; t + 4 < ntiles; t += 4) {
+        iteration(t, acc0, acc1, st2, st0);
+        iteration(t + 1, acc1, acc0, st3, st1);
+        iteration(t + 2, acc0, acc1, st0, st2);
+        iteration(t + 3, acc1, acc0, st1, st3);
+    }
+    // remaining tiles t .. ntiles-1 (1 to 4 of them); tile t's scores are in acc0
+    if (t + 1 < ntiles) {
+        iteration(t, acc0, acc1, st2, st0);
+        if (t + 2 < ntiles) {
+            iteration(t + 1, acc1, acc0, st3, st1);
+            if (t + 3 < ntiles) {
+                iteration(t + 2, acc0, acc1, st0, st2);
+                epilogue(acc1, t + 3);
+            } else {
+                epilogue(acc0, t + 2);
+            }
+        } else {
+            epilogue(acc1, t + 1);
+        }
+    } else {
+        epilogue(acc0, t);
     }
 
     // ---- merge the two half-waves that hold the same point; write the label
@@ -338,14 +387,14 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
     }
 }
 
-template <typename T, int Q, int NB, bool VEC, bool EXACT>
+template <typename T, int Q, int NB, bool VEC, bool EXACT, bool SMALLK>
 hipError_t launch_assign_t(const void* X, const void* C, const float* bias, int32_t* labels,
                            float* min_dist, int64_t B, int64_t N, int64_t K, int d,
                            hipStream_t s) {
     constexpr int ROWB = 2 * Q * 16 + 16;
     constexpr size_t lds = 2 * (size_t)kAssignBK * ROWB + 2 * kAssignBK * sizeof(float);
     constexpr int PTS = kAssignWaves * NB * 32;
-    auto kern = k_assign<T, Q, NB, VEC, EXACT>;
+    auto kern = k_assign<T, Q, NB, VEC, EXACT, SMALLK>;
     static bool attr_set = false;  // one attribute call per instantiation and process
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -369,16 +418,21 @@ hipError_t dispatch_assign(const void* X, const void* C, const float* bias, int3
     constexpr int V = 16 / sizeof(T);
     const int need = (d + 2 * V - 1) / (2 * V);  // chunks per half row
     const bool vec = (d % V) == 0;
-#define FK_ASSIGN_CASE(QQ, NBB)                                                              \
-    if (need <= QQ) {                                                                        \
-        if (vec && d == 2 * QQ * V)                                                          \
-            return launch_assign_t<T, QQ, NBB, true, true>(X, C, bias, labels, min_dist, B, N, \
-                                                           K, d, s);                         \
-        if (vec)                                                                             \
-            return launch_assign_t<T, QQ, NBB, true, false>(X, C, bias, labels, min_dist, B,   \
-                                                            N, K, d, s);                     \
-        return launch_assign_t<T, QQ, NBB, false, false>(X, C, bias, labels, min_dist, B, N,   \
-                                                         K, d, s);                           \
+#define FK_ASSIGN_CASE(QQ, NBB)                                                               \
+    if (need <= QQ) {                                                                         \
+        if (K < kAssignBK)                                                                    \
+            return vec ? launch_assign_t<T, QQ, NBB, true, false, true>(X, C, bias, labels,     \
+                                                                        min_dist, B, N, K, d, s) \
+                       : launch_assign_t<T, QQ, NBB, false, false, true>(X, C, bias, labels,    \
+                                                                         min_dist, B, N, K, d, s); \
+        if (vec && d == 2 * QQ * V)                                                           \
+            return launch_assign_t<T, QQ, NBB, true, true, false>(X, C, bias, labels, min_dist, \
+                                                                  B, N, K, d, s);             \
+        if (vec)                                                                              \
+            return launch_assign_t<T, QQ, NBB, true, false, false>(X, C, bias, labels, min_dist, \
+                                                                   B, N, K, d, s);            \
+        return launch_assign_t<T, QQ, NBB, false, false, false>(X, C, bias, labels, min_dist, B, \
+                                                                N, K, d, s);                  \
     }
     FK_ASSIGN_CASE(1, 2)
     FK_ASSIGN_CASE(2, 2)
