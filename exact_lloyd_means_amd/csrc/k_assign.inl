@@ -93,8 +93,28 @@ struct Mfma<float> {
     }
 };
 
-constexpr int kAssignWaves = 4;
 constexpr int kAssignBK = 32;  // centroids per tile (one MFMA row block)
+constexpr int kAssignWaves = 8;  // two waves per SIMD, one workgroup per CU
+constexpr int kLdsBytes = 160 * 1024;
+
+// LDS of a workgroup: optionally the X block of the next item (points x
+// padded row), two centroid tiles (rows padded by 16 bytes) and their bias.
+constexpr int assign_lds(int Q, int NB, bool prefx) {
+    return (prefx ? kAssignWaves * NB * 32 * 2 * Q * 16 : 0) + 2 * kAssignBK * (2 * Q * 16 + 16) +
+           2 * kAssignBK * 4;
+}
+// Prefetching the next item's X block through LDS (persistent workgroups)
+// measured no faster on MI355X than loading X at the item start, so it is
+// off; the path stays for experiments with other shapes.
+constexpr bool assign_prefetch_x(int Q, int NB) {
+    return false && assign_lds(Q, NB, true) <= kLdsBytes;
+}
+// Staging register sets for centroid tiles: four (loads two iterations
+// ahead of their LDS store) when a thread moves at most two chunks per
+// tile, else two (one iteration ahead).
+constexpr int assign_sets(int Q) {
+    return (kAssignBK * 2 * Q + kAssignWaves * kWave - 1) / (kAssignWaves * kWave) <= 2 ? 4 : 2;
+}
 
 // Loads 16 bytes (V elements) of row `row` starting at element e0; elements
 // at or beyond d, and rows at or beyond `rows`, read as zero.
@@ -125,58 +145,81 @@ __device__ inline u32x4 load_chunk(const T* __restrict__ base, int64_t row, int6
 //   one; seeing a centroid twice cannot change a strict-">" running argmax
 //   (same score, later in the scan), so no padding is needed.
 //
-// Pipeline per wave: the MFMAs of tile t+1 are issued before the compare /
-// select epilogue of tile t, so matrix and vector units work at the same
-// time; the global loads of tile t+2 are in flight meanwhile and land in the
-// LDS buffer tile t used.  One barrier per tile.
+// An item is a block of 8*NB*32 points of one problem.  With PREFX the
+// kernel is persistent (one workgroup per CU walks the items) and, while it
+// runs the K loop of an item, prefetches the X block of its next item into
+// LDS, one 16-byte chunk per thread per tile iteration; the block is copied
+// into registers at the item switch, so no wave waits for X from memory.
+// Without PREFX (rows too long for the LDS budget) each workgroup takes one
+// item and loads its X straight into registers.
+//
+// Pipeline per wave and item: the MFMAs of tile t+1 are issued interleaved
+// with the compare / select epilogue of tile t (sched_group_barrier); the
+// centroid tiles reach LDS through NSET staging register sets, loaded D
+// tiles ahead of use; one barrier per tile.
 template <typename T, int Q, int NB, bool VEC, bool EXACT, bool SMALLK>
 __global__ __launch_bounds__(kAssignWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __restrict__ bias,
-              int32_t* __restrict__ labels, float* __restrict__ min_dist, int64_t N, int64_t K,
-              int d) {
+              int32_t* __restrict__ labels, float* __restrict__ min_dist, int64_t B, int64_t N,
+              int64_t K, int d) {
     using M = Mfma<T>;
+    constexpr bool PREFX = assign_prefetch_x(Q, NB);
+    constexpr int NSET = assign_sets(Q);
+    constexpr int D = NSET == 2 ? 3 : 4;               // load tile t+D in iteration t
     constexpr int V = 16 / sizeof(T);
     constexpr int HR = Q * V;                          // dimensions per half row
-    constexpr int ROWB = 2 * Q * 16 + 16;              // LDS bytes per centroid row (padded)
+    constexpr int RC = 2 * Q;                          // 16-byte chunks per padded row
+    constexpr int ROWB = RC * 16 + 16;                 // LDS bytes per centroid row (padded)
     constexpr int TILEB = kAssignBK * ROWB;
-    constexpr int CHUNKS = kAssignBK * 2 * Q;          // 16-byte chunks per tile
+    constexpr int CHUNKS = kAssignBK * RC;             // 16-byte chunks per centroid tile
     constexpr int NT = kAssignWaves * kWave;
     constexpr int PER = (CHUNKS + NT - 1) / NT;
-    constexpr int PTS = kAssignWaves * NB * 32;        // points per workgroup
+    constexpr int PTS = kAssignWaves * NB * 32;        // points per item
+    constexpr int XPT = PTS * RC / NT;                 // X chunks per thread per item
+    constexpr int XB = PREFX ? PTS * RC * 16 : 0;      // LDS bytes of the X buffer
     static_assert(!EXACT || VEC, "EXACT implies VEC");
+    static_assert((PTS * RC) % NT == 0, "X chunks divide evenly");
+    static_assert(D != 2 + NSET && (D - 2) % NSET != 0, "load and store sets differ");
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    char* s_tile = smem;                                            // [2][TILEB]
-    float* s_bias = reinterpret_cast<float*>(smem + 2 * TILEB);     // [2][BK]
+    char* s_x = smem;                                               // [PTS][RC] swizzled
+    char* s_tile = smem + XB;                                       // [2][TILEB]
+    float* s_bias = reinterpret_cast<float*>(s_tile + 2 * TILEB);   // [2][BK]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;
     const int col = lane & 31;
-    const int64_t b = blockIdx.y;
-    const T* __restrict__ Xb = X + b * N * d;
-    const T* __restrict__ Cb = C + b * K * d;
-    const float* __restrict__ biasb = bias + b * K;
-    const int64_t pbase = (int64_t)blockIdx.x * PTS + (int64_t)wave * NB * 32;
+    const int K32 = (int)K;
     const int ntiles = (int)((K + kAssignBK - 1) / kAssignBK);
+    const int lastbase = SMALLK ? 0 : K32 - kAssignBK;
+    const int64_t nbpp = (N + PTS - 1) / PTS;          // items per problem
+    const int64_t items = B * nbpp;
 
-    // ---- points of this wave: resident for the whole K loop
-    u32x4 xf[NB][Q];
-    float xsq[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        xsq[nb] = 0.f;
-        const int64_t j = pbase + nb * 32 + col;
-#pragma unroll
-        for (int q = 0; q < Q; ++q) xf[nb][q] = load_chunk<T, VEC>(Xb, j, N, d, h * HR + q * V);
-    }
-    if (min_dist) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int q = 0; q < Q; ++q) xsq[nb] += M::sumsq(xf[nb][q]);
-    }
+    // ---- X block staging: chunk c of thread tid is point p, logical chunk
+    // lc of that point; LDS slot p*RC + (lc ^ (p % RC)) (conflict-free reads)
+    const int N32 = (int)N;
+    // chunk c of this thread for the item whose X rows start at Xi and whose
+    // first point is row r0 of its problem
+    auto x_load = [&](const T* Xi, int r0, int c) -> u32x4 {
+        const int g = c * NT + tid;
+        const int p = g / RC;
+        const int lc = g % RC;
+        const int row = min(r0 + p, N32 - 1);  // rows past N: any finite data
+        if constexpr (VEC) {
+            const int e0 = EXACT ? lc * V : min(lc * V, d - V);  // zeroed after the copy
+            return *reinterpret_cast<const u32x4*>(Xi + (int64_t)row * d + e0);
+        } else {
+            return load_chunk<T, false>(Xi, row, N, d, lc * V);
+        }
+    };
+    auto x_store = [&](int c, u32x4 v) {
+        const int g = c * NT + tid;
+        const int p = g / RC;
+        const int lc = g % RC;
+        *reinterpret_cast<u32x4*>(s_x + (p * RC + (lc ^ (p & (RC - 1)))) * 16) = v;
+    };
 
     // ---- centroid tile staging (registers -> LDS).  Thread tid always moves
     // the same (row, chunk) pairs of a tile, so each load is a uniform tile
@@ -186,13 +229,11 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
     // re-reads the last tile) so the loop has no branches around them.
     int crow[PER], ccol[PER];
     uint32_t goff[PER];
-    const int K32 = (int)K;
-    const int lastbase = SMALLK ? 0 : K32 - kAssignBK;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
         const int c = tid + u * NT;
-        crow[u] = c / (2 * Q);
-        ccol[u] = c % (2 * Q);
+        crow[u] = c / RC;
+        ccol[u] = c % RC;
         const int cofs = EXACT ? ccol[u] * V : min(ccol[u] * V, d - V);
         goff[u] = (uint32_t)((crow[u] * d + cofs) * (int)sizeof(T));
     }
@@ -200,189 +241,266 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
     struct Staged {
         u32x4 v[PER];
         float bias;
-    };
-    auto gload = [&](int t, Staged& st) {
-        const int tbase = tile_base(t);
-        const char* base = reinterpret_cast<const char*>(Cb + (int64_t)tbase * d);
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            if (CHUNKS % NT == 0 || u * NT + tid < CHUNKS) {
-                if constexpr (SMALLK || !VEC) {
-                    st.v[u] = load_chunk<T, VEC>(Cb, tbase + crow[u], K, d, ccol[u] * V);
-                } else {
-                    st.v[u] = *reinterpret_cast<const u32x4*>(base + goff[u]);
-                }
-            }
-        }
-        if constexpr (SMALLK) {
-            const int k = tid & (kAssignBK - 1);
-            const float v = biasb[min(k, K32 - 1)];
-            st.bias = k < K32 ? v : -INFINITY;
-        } else {
-            st.bias = biasb[tbase + (tid & (kAssignBK - 1))];
-        }
-    };
-    auto sstore = [&](int buf, const Staged& st) {
-#pragma unroll
-        for (int u = 0; u < PER; ++u)
-            if (CHUNKS % NT == 0 || u * NT + tid < CHUNKS)
-                *reinterpret_cast<u32x4*>(s_tile + buf * TILEB + crow[u] * ROWB + ccol[u] * 16) =
-                    st.v[u];
-        // every thread stores its bias value (8 identical stores per slot), so
-        // the loop body has no branch
-        s_bias[buf * kAssignBK + (tid & (kAssignBK - 1))] = st.bias;
-    };
-
-    // MFMAs of the tile in LDS buffer `buf`; the accumulators start at the
-    // bias of their rows (8g + 4h + i, g, i = 0..3).
-    auto mma = [&](int buf, floatx16 (&acc)[NB]) {
-        floatx16 bv;
-        const float* sb = s_bias + buf * kAssignBK + 4 * h;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const floatx4 v4 = *reinterpret_cast<const floatx4*>(sb + 8 * g);
-            bv[4 * g + 0] = v4[0];
-            bv[4 * g + 1] = v4[1];
-            bv[4 * g + 2] = v4[2];
-            bv[4 * g + 3] = v4[3];
-        }
-        const char* arow = s_tile + buf * TILEB + col * ROWB + h * Q * 16;
-#pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(arow + q * 16);
-#pragma unroll
-            for (int e = 0; e < M::kSteps; ++e) {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    acc[nb] = M::step(a, xf[nb][q], (q == 0 && e == 0) ? bv : acc[nb], e);
-            }
-        }
+        u32x4 x;  // one chunk of the next item's X block (PREFX)
     };
 
     float best[NB];
     int32_t bidx[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        best[nb] = -INFINITY;
-        bidx[nb] = 0;
+    u32x4 xf[NB][Q];
+    float xsq[NB];
+
+    int64_t item = blockIdx.x;
+    if (item >= items) return;
+    if constexpr (PREFX) {  // first item: its X block straight into LDS
+        const int64_t b0 = item / nbpp;
+        const T* Xi = X + b0 * N * d;
+        const int r0 = (int)(item - b0 * nbpp) * PTS;
+        for (int c = 0; c < XPT; ++c) x_store(c, x_load(Xi, r0, c));
+        __syncthreads();
     }
-    // Running (max score, lowest index).  Within a tile the candidate index is
-    // the lane's row offset 8*(r/4) + r%4 (a small inline constant, -1 = no
-    // improvement in this tile); rows ascend with r, so strict > keeps the
-    // lowest index.  The tile base is added once per tile.
-    auto epilogue = [&](const floatx16 (&acc)[NB], int t) {
-        const int32_t kb = tile_base(t);
-        float m[NB];
-        int32_t rt[NB];
+
+    for (; item < items; item += gridDim.x) {
+        const int64_t next = PREFX && item + gridDim.x < items ? item + gridDim.x : item;
+        const int64_t bn = next / nbpp;
+        const T* Xn = X + bn * N * d;                  // next item's problem
+        const int rn = (int)(next - bn * nbpp) * PTS;  // next item's first point
+        const int64_t b = item / nbpp;
+        const int64_t pbase = (item - b * nbpp) * PTS + (int64_t)wave * NB * 32;
+        const T* __restrict__ Cb = C + b * K * d;
+        const float* __restrict__ biasb = bias + b * K;
+
+        // ---- this item's points, resident in registers for the K loop
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            m[nb] = best[nb];
-            rt[nb] = -1;
-        }
-        // the NB chains are independent; interleaving them spaces each
-        // compare from the select that consumes it
+            const int p = wave * NB * 32 + nb * 32 + col;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+            for (int q = 0; q < Q; ++q) {
+                u32x4 v;
+                if constexpr (PREFX) {
+                    const int lc = h * Q + q;
+                    v = *reinterpret_cast<const u32x4*>(s_x + (p * RC + (lc ^ (p & (RC - 1)))) * 16);
+                    if (!EXACT && h * HR + q * V >= d) v = (u32x4){0u, 0u, 0u, 0u};
+                } else {
+                    v = load_chunk<T, VEC>(X + b * N * d, pbase + nb * 32 + col, N, d,
+                                           h * HR + q * V);
+                }
+                xf[nb][q] = v;
+            }
+            xsq[nb] = 0.f;
+            best[nb] = -INFINITY;
+            bidx[nb] = 0;
+        }
+        if (min_dist) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int q = 0; q < Q; ++q) xsq[nb] += M::sumsq(xf[nb][q]);
+        }
+        if constexpr (PREFX) __syncthreads();  // the X buffer may now receive the next item
+
+        auto gload = [&](int t, Staged& st) {
+            const int tbase = tile_base(t);
+            const char* base = reinterpret_cast<const char*>(Cb + (int64_t)tbase * d);
+#pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                if (CHUNKS % NT == 0 || u * NT + tid < CHUNKS) {
+                    if constexpr (SMALLK || !VEC) {
+                        st.v[u] = load_chunk<T, VEC>(Cb, tbase + crow[u], K, d, ccol[u] * V);
+                    } else {
+                        st.v[u] = *reinterpret_cast<const u32x4*>(base + goff[u]);
+                    }
+                }
+            }
+            if constexpr (SMALLK) {
+                const int k = tid & (kAssignBK - 1);
+                const float v = biasb[min(k, K32 - 1)];
+                st.bias = k < K32 ? v : -INFINITY;
+            } else {
+                st.bias = biasb[tbase + (tid & (kAssignBK - 1))];
+            }
+            // X chunk t-D of the next item rides along with tile t (chunks
+            // before 0 and past XPT-1 repeat the first / last one)
+            if constexpr (PREFX) st.x = x_load(Xn, rn, min(max(t - D, 0), XPT - 1));
+        };
+        auto sstore = [&](int buf, const Staged& st, int t) {
+#pragma unroll
+            for (int u = 0; u < PER; ++u)
+                if (CHUNKS % NT == 0 || u * NT + tid < CHUNKS)
+                    *reinterpret_cast<u32x4*>(s_tile + buf * TILEB + crow[u] * ROWB +
+                                              ccol[u] * 16) = st.v[u];
+            // every thread stores its bias value (identical stores per slot),
+            // so the loop body has no branch
+            s_bias[buf * kAssignBK + (tid & (kAssignBK - 1))] = st.bias;
+            if constexpr (PREFX) x_store(min(max(t - D, 0), XPT - 1), st.x);
+        };
+
+        // MFMAs of the tile in LDS buffer `buf`; the accumulators start at
+        // the bias of their rows (8g + 4h + i, g, i = 0..3).
+        auto mma = [&](int buf, floatx16 (&acc)[NB]) {
+            floatx16 bv;
+            const float* sb = s_bias + buf * kAssignBK + 4 * h;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const floatx4 v4 = *reinterpret_cast<const floatx4*>(sb + 8 * g);
+                bv[4 * g + 0] = v4[0];
+                bv[4 * g + 1] = v4[1];
+                bv[4 * g + 2] = v4[2];
+                bv[4 * g + 3] = v4[3];
+            }
+            const char* arow = s_tile + buf * TILEB + col * ROWB + h * Q * 16;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(arow + q * 16);
+#pragma unroll
+                for (int e = 0; e < M::kSteps; ++e) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[nb] = M::step(a, xf[nb][q], (q == 0 && e == 0) ? bv : acc[nb], e);
+                }
+            }
+        };
+
+        // Running (max score, lowest index).  Within a tile the candidate
+        // index is the lane's row offset 8*(r/4) + r%4 (a small inline
+        // constant, -1 = no improvement in this tile); rows ascend with r, so
+        // strict > keeps the lowest index.  The tile base is added once per
+        // tile.  The NB chains are independent; interleaving them spaces each
+        // compare from the select that consumes it.
+        auto epilogue = [&](const floatx16 (&acc)[NB], int t) {
+            const int32_t kb = tile_base(t);
+            float m[NB];
+            int32_t rt[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const float s = acc[nb][r];
-                // written as "keep" so both selects take the 2-operand form
-                const bool keep = !(s > m[nb]);
-                m[nb] = keep ? m[nb] : s;
-                rt[nb] = keep ? rt[nb] : 8 * (r >> 2) + (r & 3);
+                m[nb] = best[nb];
+                rt[nb] = -1;
             }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const float s = acc[nb][r];
+                    // written as "keep" so both selects take the 2-operand form
+                    const bool keep = !(s > m[nb]);
+                    m[nb] = keep ? m[nb] : s;
+                    rt[nb] = keep ? rt[nb] : 8 * (r >> 2) + (r & 3);
+                }
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                best[nb] = m[nb];
+                bidx[nb] = rt[nb] >= 0 ? kb + rt[nb] : bidx[nb];
+            }
+        };
+
+        floatx16 acc[2][NB];
+        Staged st[NSET];
+        constexpr int U = NSET == 4 ? 4 : 2;  // unroll: acc parity and set rotation repeat
+        // set holding tile j: st[j % NSET]; with two sets tile 2 reuses tile
+        // 0's set once tile 0 is in LDS
+#pragma unroll
+        for (int j = 0; j < (D < NSET ? D : NSET); ++j) gload(j, st[j]);
+        sstore(0, st[0], 0);
+#pragma unroll
+        for (int j = NSET; j < D; ++j) gload(j, st[j % NSET]);
+        __syncthreads();
+        mma(0, acc[0]);
+        sstore(1, st[1 % NSET], 1);
+        __syncthreads();
+
+        // iteration t (t + 1 < ntiles): tile t's scores are in acc[t&1],
+        // tile t+1 is in LDS buffer (t+1)&1, tile t+2 waits in its set and
+        // tile t+D is loaded.  The body is one basic block; the schedule
+        // interleaves every MFMA of tile t+1 with a few epilogue instructions
+        // of tile t, so the vector unit works while the matrix unit runs.
+        auto iteration = [&](int t, int i) {
+            gload(t + D, st[(i + D) % NSET]);
+            mma((i + 1) & 1, acc[(i + 1) & 1]);
+            epilogue(acc[i & 1], t);
+            sstore(i & 1, st[(i + 2) % NSET], t + 2);
+            constexpr int kMfma = NB * Q * M::kSteps;
+            constexpr int kValuPer = (NB * 48 + kMfma - 1) / kMfma + 1;
+            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);                       // bias + A reads
+            __builtin_amdgcn_sched_group_barrier(0x020, PER + 1 + (PREFX ? 1 : 0), 0);  // loads
+#pragma unroll
+            for (int k = 0; k < kMfma; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);  // epilogue VALU
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // next A read
+            }
+            __syncthreads();
+        };
+        int t = 0;
+        for (; t + U < ntiles; t += U) {
+#pragma unroll
+            for (int i = 0; i < U; ++i) iteration(t + i, i);
         }
+        // the last 1..U tiles: one fewer iteration, then the final epilogue
+        switch (ntiles - t) {
+            case 1:
+                epilogue(acc[0], t);
+                break;
+            case 2:
+                iteration(t, 0);
+                epilogue(acc[1], t + 1);
+                break;
+            case 3:
+                if constexpr (U >= 4) {
+                    iteration(t, 0);
+                    iteration(t + 1, 1);
+                    epilogue(acc[0], t + 2);
+                }
+                break;
+            default:
+                if constexpr (U >= 4) {
+                    iteration(t, 0);
+                    iteration(t + 1, 1);
+                    iteration(t + 2, 2);
+                    epilogue(acc[1], t + 3);
+                }
+                break;
+        }
+
+        // ---- merge the two half-waves that hold the same point; write labels
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            best[nb] = m[nb];
-            bidx[nb] = rt[nb] >= 0 ? kb + rt[nb] : bidx[nb];
-        }
-    };
-
-    // Prefetch distance: the loads of tile t+3 are issued in iteration t and
-    // reach LDS in iteration t+1, so a global load has more than a full
-    // iteration to land.
-    floatx16 acc0[NB], acc1[NB];
-    // Four staging register sets: the loads of tile t+4 are issued in
-    // iteration t and reach LDS in iteration t+2, two iterations later.
-    Staged st0, st1, st2, st3;
-    gload(0, st0);
-    gload(1, st1);
-    gload(2, st2);
-    gload(3, st3);
-    sstore(0, st0);
-    __syncthreads();
-    mma(0, acc0);
-    sstore(1, st1);
-    __syncthreads();
-
-    // iteration t (t + 1 < ntiles): tile t's scores are in accA, tile t+1 is
-    // in LDS buffer (t+1)&1, tile t+2 waits in stS (loaded two iterations
-    // ago) and stL receives tile t+4.
-    // The body is one basic block; the schedule below interleaves every MFMA
-    // of tile t+1 with about six epilogue instructions of tile t, so the
-    // vector unit works while the matrix unit runs.  Loads and stores past
-    // the last tile move unused data.
-    auto iteration = [&](int t, floatx16 (&accA)[NB], floatx16 (&accB)[NB], Staged& stS,
-                         Staged& stL) {
-        gload(t + 4, stL);
-        mma((t + 1) & 1, accB);
-        epilogue(accA, t);
-        sstore(t & 1, stS);
-        constexpr int kMfma = NB * Q * M::kSteps;
-        constexpr int kValuPer = (NB * 48 + kMfma - 1) / kMfma + 1;
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // bias + first A fragment reads
-        __builtin_amdgcn_sched_group_barrier(0x020, PER + 1, 0);  // global loads, tile t+4
-#pragma unroll
-        for (int i = 0; i < kMfma; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);  // epilogue VALU
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // next A fragment read
-        }
-        __syncthreads();
-    };
-    // set holding tile j: st[j % 4]; iteration t stores tile t+2 and loads t+4
-    int t = 0;
-    for (; t + 4 < ntiles; t += 4) {
-        iteration(t, acc0, acc1, st2, st0);
-        iteration(t + 1, acc1, acc0, st3, st1);
-        iteration(t + 2, acc0, acc1, st0, st2);
-        iteration(t + 3, acc1, acc0, st1, st3);
-    }
-    // remaining tiles t .. ntiles-1 (1 to 4 of them); tile t's scores are in acc0
-    if (t + 1 < ntiles) {
-        iteration(t, acc0, acc1, st2, st0);
-        if (t + 2 < ntiles) {
-            iteration(t + 1, acc1, acc0, st3, st1);
-            if (t + 3 < ntiles) {
-                iteration(t + 2, acc0, acc1, st0, st2);
-                epilogue(acc1, t + 3);
-            } else {
-                epilogue(acc0, t + 2);
+            float sc = best[nb];
+            int32_t i = bidx[nb] + 4 * h;
+            const float so = __shfl_xor(sc, 32);
+            const int32_t io = __shfl_xor(i, 32);
+            if (so > sc || (so == sc && io < i)) {
+                sc = so;
+                i = io;
             }
-        } else {
-            epilogue(acc1, t + 1);
+            const float xx = xsq[nb] + __shfl_xor(xsq[nb], 32);
+            const int64_t j = pbase + nb * 32 + col;
+            if (h == 0 && j < N) {
+                labels[b * N + j] = i;
+                if (min_dist) min_dist[b * N + j] = xx - 2.f * sc;
+            }
         }
-    } else {
-        epilogue(acc0, t);
-    }
 
-    // ---- merge the two half-waves that hold the same point; write the label
+        if constexpr (PREFX) {
+            // ---- complete the next item's X block.  Tile j carries X chunk
+            // j-D.  Iterations 0 .. ntiles-2 loaded tiles up to ntiles-2+D
+            // and stored tiles up to ntiles, so the chunks of tiles ntiles+1
+            // .. ntiles+D-2 still sit in their sets and chunks from ntiles-1
+            // on were never loaded.
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        float s = best[nb];
-        int32_t i = bidx[nb] + 4 * h;
-        const float so = __shfl_xor(s, 32);
-        const int32_t io = __shfl_xor(i, 32);
-        if (so > s || (so == s && io < i)) {
-            s = so;
-            i = io;
-        }
-        const float xx = xsq[nb] + __shfl_xor(xsq[nb], 32);
-        const int64_t j = pbase + nb * 32 + col;
-        if (h == 0 && j < N) {
-            labels[b * N + j] = i;
-            if (min_dist) min_dist[b * N + j] = xx - 2.f * s;
+            for (int j = 1; j <= D - 2; ++j) {
+                const int tj = ntiles + j;      // tile whose set holds the chunk
+                const int c = tj - D;
+                if (c >= 0 && c < XPT) {
+                    const int si = tj % NSET;
+                    u32x4 v = st[0].x;
+#pragma unroll
+                    for (int k = 1; k < NSET; ++k)
+                        if (si == k) v = st[k].x;
+                    x_store(c, v);
+                }
+            }
+            for (int c = max(ntiles - 1, 0); c < XPT; ++c) x_store(c, x_load(Xn, rn, c));
+            __syncthreads();
         }
     }
 }
@@ -391,21 +509,30 @@ template <typename T, int Q, int NB, bool VEC, bool EXACT, bool SMALLK>
 hipError_t launch_assign_t(const void* X, const void* C, const float* bias, int32_t* labels,
                            float* min_dist, int64_t B, int64_t N, int64_t K, int d,
                            hipStream_t s) {
-    constexpr int ROWB = 2 * Q * 16 + 16;
-    constexpr size_t lds = 2 * (size_t)kAssignBK * ROWB + 2 * kAssignBK * sizeof(float);
+    constexpr bool prefx = assign_prefetch_x(Q, NB);
+    constexpr int lds = assign_lds(Q, NB, prefx);
+    static_assert(lds <= kLdsBytes, "LDS budget");
     constexpr int PTS = kAssignWaves * NB * 32;
     auto kern = k_assign<T, Q, NB, VEC, EXACT, SMALLK>;
     static bool attr_set = false;  // one attribute call per instantiation and process
+    static int cus = 0;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        int dev = 0;
+        e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    dim3 grid((unsigned)((N + PTS - 1) / PTS), (unsigned)B);
-    hipLaunchKernelGGL(kern, grid, dim3(kAssignWaves * kWave), lds, s,
+    const int64_t items = B * ((N + PTS - 1) / PTS);
+    // persistent: one workgroup per CU; otherwise one workgroup per item
+    const int64_t grid = prefx ? (items < cus ? items : cus) : items;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kAssignWaves * kWave), lds, s,
                        static_cast<const T*>(X), static_cast<const T*>(C), bias, labels, min_dist,
-                       N, K, d);
+                       B, N, K, d);
     return hipGetLastError();
 }
 
