@@ -79,8 +79,6 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int64_t kMaxIndex = 2147483646;  // N and K must leave room for N + 1 / K + 1 in int32
 constexpr int64_t kMaxD = 65536;
 
-// Largest d the register-resident assign kernel supports for a dtype.
-int64_t max_assign_d(int dtype) { return dtype == FK_F32 ? 256 : 512; }
 
 fk_status check_problem(const fk_problem* p) {
     if (!p) return fail(FK_EINVAL, "problem is NULL");
@@ -113,12 +111,7 @@ fk_status check_ws(const fk_problem& p, void* ws, size_t ws_bytes, Workspace* ou
     return FK_OK;
 }
 
-fk_status check_assign_d(const fk_problem& p) {
-    if (p.d > max_assign_d(p.dtype))
-        return fail(FK_EUNSUPPORTED, "assign supports d <= %lld for this dtype (d=%lld)",
-                    (long long)max_assign_d(p.dtype), (long long)p.d);
-    return FK_OK;
-}
+fk_status check_assign_d(const fk_problem&) { return FK_OK; }
 
 #define FK_CHECK(expr)                    \
     do {                                  \

@@ -48,7 +48,7 @@ def test_golden_tie_case(dt):
 
 SHAPES_INT = [(1, 1, 1, 1), (2, 37, 5, 3), (3, 300, 70, 2), (1, 1000, 33, 3), (2, 129, 1, 1),
               (1, 5, 9, 2), (2, 700, 64, 16), (1, 513, 100, 127), (2, 300, 40, 128),
-              (1, 257, 65, 129), (1, 200, 50, 256)]
+              (1, 257, 65, 129), (1, 200, 50, 256), (1, 300, 300, 1024), (1, 100, 40, 600)]
 
 
 @pytest.mark.parametrize("dt", DT)
@@ -57,8 +57,6 @@ def test_integer_ties_exact(dt, shape):
     """Integer inputs: every product and partial sum is exact in fp32, so the
     GPU must reproduce the lowest-index tie rule bit for bit (no exclusions)."""
     B, N, K, d = shape
-    if dt == "f32" and d > 256:
-        pytest.skip("fp32 resident assign covers d <= 256")
     Xi, Ci, X, C = int_case(B, N, K, d, dt, seed=hash(shape) % 1000)
     labels, md = run_assign(X, C)
     lab, d1, _ = oracle.assign(Xi.astype(np.float64), Ci.astype(np.float64))
@@ -66,7 +64,7 @@ def test_integer_ties_exact(dt, shape):
     assert np.array_equal(md.cpu().numpy().astype(np.float64), d1)
 
 
-CFG_SHRUNK = {1: dict(), 2: dict(B=2, N=8192), 3: dict(N=16384)}
+CFG_SHRUNK = {1: dict(), 2: dict(B=2, N=8192), 3: dict(N=16384), 4: dict(N=3000, K=1100)}
 
 
 @pytest.mark.parametrize("cfg", sorted(CFG_SHRUNK))
@@ -81,15 +79,16 @@ def test_config_inputs(cfg):
 
 EDGE = [(1, 1, 1, 1), (1, 31, 2, 2), (2, 33, 31, 3), (1, 257, 33, 8), (3, 1000, 100, 17),
         (1, 300, 64, 64), (1, 129, 100, 127), (2, 500, 97, 128), (1, 250, 130, 129),
-        (1, 200, 70, 200), (1, 130, 40, 256), (1, 100, 35, 300), (1, 70, 33, 512)]
+        (1, 200, 70, 200), (1, 130, 40, 256), (1, 100, 35, 300), (1, 70, 33, 512),
+        # rows longer than the register-resident limit: split-d kernel
+        (1, 300, 70, 513), (2, 257, 300, 1024), (1, 100, 40, 1000), (1, 64, 33, 1100),
+        (1, 600, 520, 640)]
 
 
 @pytest.mark.parametrize("dt", DT)
 @pytest.mark.parametrize("shape", EDGE, ids=lambda s: "x".join(map(str, s)))
 def test_edge_shapes_random(dt, shape):
     B, N, K, d = shape
-    if dt == "f32" and d > 256:
-        pytest.skip("fp32 resident assign covers d <= 256")
     g = torch.Generator().manual_seed(B * 1000003 + N * 1009 + K * 31 + d)
     X = torch.randn((B, N, d), generator=g).to(TORCH[dt]).cuda()
     C = (torch.randn((B, K, d), generator=g) * 1.2).to(TORCH[dt]).cuda()
