@@ -49,6 +49,8 @@ _SIG = {
     "fk_update": ([_PP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "fk_lloyd": ([_PP, _P, _P, _P, _P, ctypes.c_int, ctypes.c_float,
                   ctypes.POINTER(ctypes.c_int), _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "fk_lloyd_streamed": ([_PP, _P, ctypes.c_int64, _P, _P, _P, ctypes.c_int, _P, ctypes.c_size_t,
+                           _P, _P], ctypes.c_int),
     "fk_error_count": ([_PP, _P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int64), _P],
                        ctypes.c_int),
 }
@@ -177,6 +179,22 @@ def fk_lloyd(X: torch.Tensor, C: torch.Tensor, labels: torch.Tensor, counts: tor
                         int(max_iters), float(tol), ctypes.byref(n) if want_n_iter else None,
                         _ptr(ws), ws.numel(), _stream(stream)), "fk_lloyd")
     return n.value if want_n_iter else None
+
+
+def fk_lloyd_streamed(X_host: torch.Tensor, C: torch.Tensor, labels: torch.Tensor,
+                      counts: torch.Tensor, max_iters: int, chunk_points: int,
+                      ws: torch.Tensor | None = None, compute_stream=None, copy_stream=None) -> None:
+    """Lloyd iterations on a pinned host tensor X_host (B, N, d), streamed to
+    the GPU in chunks of chunk_points points; C, labels, counts on the GPU."""
+    p = _problem_from(X_host, C.shape[1])
+    if not X_host.is_pinned():
+        raise ValueError("X_host must be a pinned CPU tensor (pin_memory=True)")
+    ws = workspace(p, C.device, chunk_points) if ws is None else ws
+    cs = _stream(compute_stream)
+    xs = _stream(copy_stream) if copy_stream is not None else cs
+    _check(lib.fk_lloyd_streamed(ctypes.byref(p), _ptr(X_host), int(chunk_points), _ptr(C),
+                                 _ptr(labels), _ptr(counts), int(max_iters), _ptr(ws), ws.numel(),
+                                 cs, xs), "fk_lloyd_streamed")
 
 
 def fk_error_count(p: Problem, ws: torch.Tensor, stream=None) -> int:

@@ -48,6 +48,30 @@ Workspace workspace_layout(const fk_problem& p, char* base) {
     return w;
 }
 
+StreamWorkspace stream_workspace_layout(const fk_problem& p, int64_t chunk, char* base) {
+    StreamWorkspace w{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) -> char* {
+        char* at = base ? base + o : nullptr;
+        o = align256(o + bytes);
+        return at;
+    };
+    const size_t B = (size_t)p.B, K = (size_t)p.K, d = (size_t)p.d, c = (size_t)chunk;
+    const size_t es = (size_t)dtype_size(p.dtype);
+    w.xbuf[0] = take(c * d * es);
+    w.xbuf[1] = take(c * d * es);
+    w.bias = reinterpret_cast<float*>(take(B * K * sizeof(float)));
+    w.lowp = p.dtype == FK_F32 ? nullptr : take(B * K * d * es);
+    w.sums = reinterpret_cast<float*>(take(B * K * d * sizeof(float)));
+    w.ccounts = reinterpret_cast<int32_t*>(take(K * sizeof(int32_t)));
+    w.offsets = reinterpret_cast<int32_t*>(take((K + 1) * sizeof(int32_t)));
+    w.cursor = reinterpret_cast<int32_t*>(take(K * sizeof(int32_t)));
+    w.sorted_idx = reinterpret_cast<int32_t*>(take(c * sizeof(int32_t)));
+    w.flags = reinterpret_cast<uint32_t*>(take(256));
+    w.total = o;
+    return w;
+}
+
 }  // namespace fk
 
 namespace {
@@ -153,8 +177,11 @@ const char* fk_last_error(void) { return g_err; }
 fk_status fk_workspace_size(const fk_problem* p, int64_t chunk_points, size_t* bytes) {
     FK_CHECK(check_problem(p));
     if (!bytes) return fail(FK_EINVAL, "bytes is NULL");
-    if (chunk_points != 0) return fail(FK_EUNSUPPORTED, "streamed workspace not available");
-    *bytes = workspace_layout(*p, nullptr).total;
+    if (chunk_points < 0) return fail(FK_EINVAL, "chunk_points must be >= 0");
+    if (chunk_points > kMaxIndex) return fail(FK_EUNSUPPORTED, "chunk_points too large");
+    *bytes = chunk_points == 0
+                 ? workspace_layout(*p, nullptr).total
+                 : stream_workspace_layout(*p, chunk_points < p->N ? chunk_points : p->N, nullptr).total;
     return FK_OK;
 }
 
@@ -299,6 +326,102 @@ fk_status fk_lloyd(const fk_problem* p, const void* X, float* C, int32_t* labels
     }
     if (n_iter) *n_iter = it;
     return FK_OK;
+}
+
+fk_status fk_lloyd_streamed(const fk_problem* p, const void* X_host, int64_t chunk_points,
+                            float* C, int32_t* labels, int32_t* counts, int max_iters, void* ws,
+                            size_t ws_bytes, void* compute_stream, void* copy_stream) {
+    FK_CHECK(check_problem(p));
+    if (!X_host) return fail(FK_EINVAL, "X_host is NULL");
+    FK_CHECK(check_ptr(C, "C"));
+    FK_CHECK(check_ptr(labels, "labels"));
+    FK_CHECK(check_ptr(counts, "counts"));
+    if (chunk_points < 1) return fail(FK_EINVAL, "chunk_points must be >= 1");
+    if (chunk_points > kMaxIndex) return fail(FK_EUNSUPPORTED, "chunk_points too large");
+    if (max_iters < 1) return fail(FK_EINVAL, "max_iters must be >= 1");
+    if (p->d > 1024) return fail(FK_EUNSUPPORTED, "update supports d <= 1024");
+    const int64_t chunk = chunk_points < p->N ? chunk_points : p->N;
+    const StreamWorkspace need = stream_workspace_layout(*p, chunk, nullptr);
+    if (!ws) return fail(FK_EWORKSPACE, "workspace is NULL");
+    if (!aligned16(ws)) return fail(FK_EINVAL, "workspace is not 16-byte aligned");
+    if (ws_bytes < need.total)
+        return fail(FK_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need.total);
+    // the source must be pinned host memory for asynchronous copies
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, X_host) != hipSuccess || attr.type != hipMemoryTypeHost) {
+        (void)hipGetLastError();
+        return fail(FK_EINVAL, "X_host must be pinned host memory (hipHostMalloc)");
+    }
+    const StreamWorkspace w = stream_workspace_layout(*p, chunk, static_cast<char*>(ws));
+    hipStream_t cs = static_cast<hipStream_t>(compute_stream);
+    hipStream_t xs = static_cast<hipStream_t>(copy_stream);
+    const int64_t B = p->B, N = p->N, K = p->K, d = p->d;
+    const int64_t rows = B * K;
+    const size_t es = (size_t)dtype_size(p->dtype);
+    const int64_t nchunk = (N + chunk - 1) / chunk;
+
+    hipEvent_t copied[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr};
+    fk_status st = FK_OK;
+    for (int i = 0; i < 2 && st == FK_OK; ++i) {
+        if (hipEventCreateWithFlags(&copied[i], hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&done[i], hipEventDisableTiming) != hipSuccess)
+            st = fail(FK_EHOST, "cannot create events");
+    }
+    // the copy stream starts after everything already queued on the compute stream
+    if (st == FK_OK && xs != cs) {
+        hipError_t e = hipEventRecord(done[0], cs);
+        if (e == hipSuccess) e = hipStreamWaitEvent(xs, done[0], 0);
+        if (e != hipSuccess) st = hip_fail(e, "order streams");
+    }
+    auto body = [&]() -> fk_status {
+        const int dt = p->dtype;
+        FK_TRY(launch_fill_u32(w.flags, 64, 0u, cs), "clear flags");
+        FK_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(w.sums), rows * d, 0u, cs), "clear sums");
+        FK_TRY(launch_prepare(dt, C, w.lowp, w.bias, rows, (int)d, cs), "prepare centroids");
+        const void* Cq = dt == FK_F32 ? static_cast<const void*>(C) : w.lowp;
+        int64_t seq = 0;  // chunk sequence number across iterations
+        for (int it = 0; it < max_iters; ++it) {
+            FK_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(counts), rows, 0u, cs), "clear counts");
+            for (int64_t b = 0; b < B; ++b) {
+                const char* Cqb = static_cast<const char*>(Cq) + (size_t)(b * K * d) * es;
+                for (int64_t c = 0; c < nchunk; ++c, ++seq) {
+                    const int buf = (int)(seq & 1);
+                    const int64_t i0 = c * chunk;
+                    const int64_t n = (N - i0) < chunk ? (N - i0) : chunk;
+                    // copy stream: wait until the compute stream released this buffer
+                    if (seq >= 2) FK_TRY(hipStreamWaitEvent(xs, done[buf], 0), "wait buffer");
+                    const char* src = static_cast<const char*>(X_host) + (size_t)((b * N + i0) * d) * es;
+                    FK_TRY(hipMemcpyAsync(w.xbuf[buf], src, (size_t)(n * d) * es, hipMemcpyHostToDevice, xs),
+                           "copy chunk");
+                    FK_TRY(hipEventRecord(copied[buf], xs), "record copy");
+                    // compute stream: assign, sort and segment sums of this chunk
+                    FK_TRY(hipStreamWaitEvent(cs, copied[buf], 0), "wait copy");
+                    int32_t* lab = labels + b * N + i0;
+                    FK_TRY(launch_assign(dt, w.xbuf[buf], Cqb, w.bias + b * K, lab, nullptr, 1, n, K,
+                                         (int)d, cs),
+                           "assign");
+                    FK_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(w.ccounts), K, 0u, cs), "clear chunk counts");
+                    FK_TRY(launch_histogram(lab, w.ccounts, w.flags, 1, n, K, cs), "histogram");
+                    FK_TRY(launch_scan(w.ccounts, w.offsets, w.cursor, 1, K, cs), "scan");
+                    FK_TRY(launch_scatter(lab, w.cursor, w.sorted_idx, 1, n, K, cs), "scatter");
+                    FK_TRY(launch_segment_sums(dt, w.xbuf[buf], w.sorted_idx, w.offsets, w.sums + b * K * d,
+                                               1, n, K, (int)d, cs),
+                           "segment sums");
+                    FK_TRY(launch_add_i32(counts + b * K, w.ccounts, K, cs), "add counts");
+                    FK_TRY(hipEventRecord(done[buf], cs), "record done");
+                }
+            }
+            FK_TRY(launch_finalize(dt, w.sums, counts, C, C, w.lowp, w.bias, nullptr, rows, (int)d, cs),
+                   "finalize");
+        }
+        return FK_OK;
+    };
+    if (st == FK_OK) st = body();
+    for (int i = 0; i < 2; ++i) {
+        if (copied[i]) (void)hipEventDestroy(copied[i]);
+        if (done[i]) (void)hipEventDestroy(done[i]);
+    }
+    return st;
 }
 
 fk_status fk_error_count(const fk_problem* p, const void* ws, size_t ws_bytes, int64_t* count,

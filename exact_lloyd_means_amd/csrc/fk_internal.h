@@ -35,8 +35,28 @@ struct Workspace {
 
 Workspace workspace_layout(const fk_problem& p, char* base);
 
+// Workspace of the streamed path: two chunk buffers of X, the sort scratch
+// of one chunk, and the per-problem sums, bias and low-precision centroids.
+struct StreamWorkspace {
+    void* xbuf[2];       // [chunk][d] problem dtype
+    float* bias;         // [B][K]
+    void* lowp;          // [B][K][d] (16-bit dtypes)
+    float* sums;         // [B][K][d]
+    int32_t* ccounts;    // [K]   counts of one chunk
+    int32_t* offsets;    // [K+1] segment starts of one chunk
+    int32_t* cursor;     // [K]
+    int32_t* sorted_idx; // [chunk]
+    uint32_t* flags;     // [0] out-of-range labels
+    size_t total;
+};
+
+StreamWorkspace stream_workspace_layout(const fk_problem& p, int64_t chunk, char* base);
+
 // ---- launchers (return hipSuccess or the launch error) ----------------------
 hipError_t launch_fill_u32(uint32_t* ptr, int64_t n, uint32_t value, hipStream_t s);
+
+// dst[i] += src[i]
+hipError_t launch_add_i32(int32_t* dst, const int32_t* src, int64_t n, hipStream_t s);
 
 hipError_t launch_centroid_bias(int dtype, const void* C, float* bias, int64_t rows, int d,
                                 hipStream_t s);

@@ -53,6 +53,12 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
         p[i] = v;
 }
 
+__global__ void k_add_i32(int32_t* __restrict__ dst, const int32_t* __restrict__ src, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        dst[i] += src[i];
+}
+
 // bias[row] = -0.5 * sum_j C[row][j]^2 in fp32 (one wave per centroid row)
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_centroid_bias(const T* __restrict__ C,
@@ -378,6 +384,13 @@ hipError_t launch_fill_u32(uint32_t* ptr, int64_t n, uint32_t value, hipStream_t
     if (n <= 0) return hipSuccess;
     const int64_t blocks = min((n + kBlock - 1) / kBlock, (int64_t)4096);
     hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(kBlock), 0, s, ptr, n, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_add_i32(int32_t* dst, const int32_t* src, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = min((n + kBlock - 1) / kBlock, (int64_t)1024);
+    hipLaunchKernelGGL(k_add_i32, dim3((unsigned)blocks), dim3(kBlock), 0, s, dst, src, n);
     return hipGetLastError();
 }
 

@@ -92,7 +92,8 @@ const char* fk_last_error(void);
 /*
  * fk_workspace_size -- bytes of device workspace the other calls need for
  * problem *p.  chunk_points = 0: fk_assign, fk_sort_labels, fk_update and
- * fk_lloyd.  The size has no N x K term: the distance matrix is never stored
+ * fk_lloyd; chunk_points > 0: fk_lloyd_streamed with chunks of that many
+ * points (capped at N).  The size has no N x K term: the distance matrix is never stored
  * (papernotes.org notes, 关键设计 1: IO falls from O(NK) to O(Nd + Kd)).
  * *bytes (host) receives the size.
  */
@@ -176,6 +177,29 @@ fk_status fk_update(const fk_problem* p, const void* X, const int32_t* labels,
 fk_status fk_lloyd(const fk_problem* p, const void* X, float* C, int32_t* labels,
                    int32_t* counts, int max_iters, float tol, int* n_iter, void* ws,
                    size_t ws_bytes, void* stream);
+
+/*
+ * fk_lloyd_streamed -- fk_lloyd for inputs held in host memory
+ * (papernotes.org notes, 关键设计 3: chunks of the point set move from host
+ * to device on asynchronous streams, ping-pong, overlapped with the assign
+ * and update work, so device memory no longer bounds N).
+ *   X_host [B][N][d] problem dtype, PINNED host memory (hipHostMalloc);
+ *   chunk_points points per chunk (the last chunk of a problem may be
+ *     shorter); the workspace holds two chunk buffers, see
+ *     fk_workspace_size(p, chunk_points, ...);
+ *   C, labels, counts as in fk_lloyd (device memory); max_iters iterations
+ *     are run (no tolerance stop);
+ *   compute_stream runs the kernels, copy_stream the host-to-device copies
+ *     (they may be the same stream, then nothing overlaps).
+ * Per iteration each chunk is copied once; chunk j+1 is copied while chunk
+ * j is assigned and reduced; sums and counts accumulate over all chunks and
+ * the centroids are finalized once per iteration.  Work already queued on
+ * compute_stream completes before the first copy starts.  Returns FK_EHOST
+ * when stream events cannot be created.
+ */
+fk_status fk_lloyd_streamed(const fk_problem* p, const void* X_host, int64_t chunk_points,
+                            float* C, int32_t* labels, int32_t* counts, int max_iters, void* ws,
+                            size_t ws_bytes, void* compute_stream, void* copy_stream);
 
 /*
  * fk_error_count -- number of out-of-range labels skipped by the most recent
