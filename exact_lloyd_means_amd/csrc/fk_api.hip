@@ -40,6 +40,7 @@ Workspace workspace_layout(const fk_problem& p, char* base) {
     w.offsets = reinterpret_cast<int32_t*>(take(B * (K + 1) * sizeof(int32_t)));
     w.cursor = reinterpret_cast<int32_t*>(take(B * K * sizeof(int32_t)));
     w.sorted_idx = reinterpret_cast<int32_t*>(take(B * N * sizeof(int32_t)));
+    w.sorted_lab = reinterpret_cast<int32_t*>(take(B * N * sizeof(int32_t)));
     w.sums = reinterpret_cast<float*>(take(B * K * d * sizeof(float)));
     w.counts = reinterpret_cast<int32_t*>(take(B * K * sizeof(int32_t)));
     w.lowp = p.dtype == FK_F32 ? nullptr : take(B * K * d * (size_t)dtype_size(p.dtype));
@@ -67,6 +68,7 @@ StreamWorkspace stream_workspace_layout(const fk_problem& p, int64_t chunk, char
     w.offsets = reinterpret_cast<int32_t*>(take((K + 1) * sizeof(int32_t)));
     w.cursor = reinterpret_cast<int32_t*>(take(K * sizeof(int32_t)));
     w.sorted_idx = reinterpret_cast<int32_t*>(take(c * sizeof(int32_t)));
+    w.sorted_lab = reinterpret_cast<int32_t*>(take(c * sizeof(int32_t)));
     w.flags = reinterpret_cast<uint32_t*>(take(256));
     w.total = o;
     return w;
@@ -145,12 +147,12 @@ fk_status check_assign_d(const fk_problem&) { return FK_OK; }
 
 // Counting-sort argsort of the labels: counts, offsets, cursor, sorted_idx.
 fk_status enqueue_sort(const fk_problem& p, const int32_t* labels, int32_t* counts,
-                       int32_t* offsets, int32_t* cursor, int32_t* sorted_idx, uint32_t* flags,
-                       hipStream_t s) {
+                       int32_t* offsets, int32_t* cursor, int32_t* sorted_idx,
+                       int32_t* sorted_lab, uint32_t* flags, hipStream_t s) {
     FK_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(counts), p.B * p.K, 0u, s), "clear counts");
     FK_TRY(launch_histogram(labels, counts, flags, p.B, p.N, p.K, s), "histogram");
     FK_TRY(launch_scan(counts, offsets, cursor, p.B, p.K, s), "scan");
-    FK_TRY(launch_scatter(labels, cursor, sorted_idx, p.B, p.N, p.K, s), "scatter");
+    FK_TRY(launch_scatter(labels, cursor, sorted_idx, sorted_lab, p.B, p.N, p.K, s), "scatter");
     return FK_OK;
 }
 
@@ -238,7 +240,7 @@ fk_status fk_sort_labels(const fk_problem* p, const int32_t* labels, int32_t* co
     FK_CHECK(check_ws(*p, ws, ws_bytes, &w));
     hipStream_t s = static_cast<hipStream_t>(stream);
     FK_TRY(launch_fill_u32(w.flags, 64, 0u, s), "clear flags");
-    return enqueue_sort(*p, labels, counts, offsets, w.cursor, sorted_idx, w.flags, s);
+    return enqueue_sort(*p, labels, counts, offsets, w.cursor, sorted_idx, nullptr, w.flags, s);
 }
 
 fk_status fk_update(const fk_problem* p, const void* X, const int32_t* labels,
@@ -260,9 +262,10 @@ fk_status fk_update(const fk_problem* p, const void* X, const int32_t* labels,
     const int64_t rows = p->B * p->K;
     FK_TRY(launch_fill_u32(w.flags, 64, 0u, s), "clear flags");
     FK_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(w.sums), rows * p->d, 0u, s), "clear sums");
-    FK_CHECK(enqueue_sort(*p, labels, counts, w.offsets, w.cursor, w.sorted_idx, w.flags, s));
-    FK_TRY(launch_segment_sums(p->dtype, X, w.sorted_idx, w.offsets, w.sums, p->B, p->N, p->K,
-                               (int)p->d, s),
+    FK_CHECK(enqueue_sort(*p, labels, counts, w.offsets, w.cursor, w.sorted_idx, w.sorted_lab,
+                          w.flags, s));
+    FK_TRY(launch_segment_sums(p->dtype, X, w.sorted_idx, w.sorted_lab, w.offsets, w.sums, p->B,
+                               p->N, p->K, (int)p->d, s),
            "segment sums");
     if (p->dtype == FK_F32 && C_next_lowp) {
         FK_TRY(launch_finalize(p->dtype, w.sums, counts, C_prev, C_next, nullptr, nullptr, nullptr,
@@ -306,9 +309,10 @@ fk_status fk_lloyd(const fk_problem* p, const void* X, float* C, int32_t* labels
         FK_TRY(launch_assign(p->dtype, X, Cq, w.bias, labels, nullptr, p->B, p->N, p->K,
                              (int)p->d, s),
                "assign");
-        FK_CHECK(enqueue_sort(*p, labels, counts, w.offsets, w.cursor, w.sorted_idx, w.flags, s));
-        FK_TRY(launch_segment_sums(p->dtype, X, w.sorted_idx, w.offsets, w.sums, p->B, p->N, p->K,
-                                   (int)p->d, s),
+        FK_CHECK(enqueue_sort(*p, labels, counts, w.offsets, w.cursor, w.sorted_idx, w.sorted_lab,
+                              w.flags, s));
+        FK_TRY(launch_segment_sums(p->dtype, X, w.sorted_idx, w.sorted_lab, w.offsets, w.sums,
+                                   p->B, p->N, p->K, (int)p->d, s),
                "segment sums");
         FK_TRY(launch_finalize(p->dtype, w.sums, counts, C, C, w.lowp, w.bias,
                                sync ? w.flags + 1 : nullptr, rows, (int)p->d, s),
@@ -403,9 +407,10 @@ fk_status fk_lloyd_streamed(const fk_problem* p, const void* X_host, int64_t chu
                     FK_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(w.ccounts), K, 0u, cs), "clear chunk counts");
                     FK_TRY(launch_histogram(lab, w.ccounts, w.flags, 1, n, K, cs), "histogram");
                     FK_TRY(launch_scan(w.ccounts, w.offsets, w.cursor, 1, K, cs), "scan");
-                    FK_TRY(launch_scatter(lab, w.cursor, w.sorted_idx, 1, n, K, cs), "scatter");
-                    FK_TRY(launch_segment_sums(dt, w.xbuf[buf], w.sorted_idx, w.offsets, w.sums + b * K * d,
-                                               1, n, K, (int)d, cs),
+                    FK_TRY(launch_scatter(lab, w.cursor, w.sorted_idx, w.sorted_lab, 1, n, K, cs),
+                           "scatter");
+                    FK_TRY(launch_segment_sums(dt, w.xbuf[buf], w.sorted_idx, w.sorted_lab, w.offsets,
+                                               w.sums + b * K * d, 1, n, K, (int)d, cs),
                            "segment sums");
                     FK_TRY(launch_add_i32(counts + b * K, w.ccounts, K, cs), "add counts");
                     FK_TRY(hipEventRecord(done[buf], cs), "record done");

@@ -26,6 +26,7 @@ struct Workspace {
     int32_t* offsets;    // [B][K+1] segment starts of the sorted labels
     int32_t* cursor;     // [B][K]   scatter cursors
     int32_t* sorted_idx; // [B][N]   argsort of the labels
+    int32_t* sorted_lab; // [B][N]   label at each sorted position
     float* sums;         // [B][K][d] fp32 segment sums
     int32_t* counts;     // [B][K]   counts when the caller passes none
     void* lowp;          // [B][K][d] centroids in the problem dtype (16-bit dtypes)
@@ -46,6 +47,7 @@ struct StreamWorkspace {
     int32_t* offsets;    // [K+1] segment starts of one chunk
     int32_t* cursor;     // [K]
     int32_t* sorted_idx; // [chunk]
+    int32_t* sorted_lab; // [chunk]
     uint32_t* flags;     // [0] out-of-range labels
     size_t total;
 };
@@ -76,12 +78,13 @@ hipError_t launch_histogram(const int32_t* labels, int32_t* counts, uint32_t* fl
 hipError_t launch_scan(const int32_t* counts, int32_t* offsets, int32_t* cursor, int64_t B,
                        int64_t K, hipStream_t s);
 
-hipError_t launch_scatter(const int32_t* labels, int32_t* cursor, int32_t* sorted_idx, int64_t B,
-                          int64_t N, int64_t K, hipStream_t s);
+// sorted_lab may be NULL
+hipError_t launch_scatter(const int32_t* labels, int32_t* cursor, int32_t* sorted_idx,
+                          int32_t* sorted_lab, int64_t B, int64_t N, int64_t K, hipStream_t s);
 
 hipError_t launch_segment_sums(int dtype, const void* X, const int32_t* sorted_idx,
-                               const int32_t* offsets, float* sums, int64_t B, int64_t N,
-                               int64_t K, int d, hipStream_t s);
+                               const int32_t* sorted_lab, const int32_t* offsets, float* sums,
+                               int64_t B, int64_t N, int64_t K, int d, hipStream_t s);
 
 // C_next = sums / counts (or C_prev when empty); optional low-precision copy,
 // bias of the copy, squared-move maximum; clears the sums.

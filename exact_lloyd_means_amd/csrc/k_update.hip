@@ -167,10 +167,12 @@ __global__ __launch_bounds__(kBlock) void k_scan(const int32_t* __restrict__ cou
     if (threadIdx.x == kBlock - 1) off[K] = s[kBlock - 1];
 }
 
-// sorted_idx[b][pos] = i with pos inside label a_i's segment
+// sorted_idx[b][pos] = i with pos inside label a_i's segment; sorted_lab
+// (optional) receives the label at each sorted position
 __global__ __launch_bounds__(kBlock) void k_scatter(const int32_t* __restrict__ labels,
                                                     int32_t* __restrict__ cursor,
-                                                    int32_t* __restrict__ sorted_idx, int64_t N,
+                                                    int32_t* __restrict__ sorted_idx,
+                                                    int32_t* __restrict__ sorted_lab, int64_t N,
                                                     int64_t K, int use_lds) {
     extern __shared__ int32_t s_base[];
     const int64_t b = blockIdx.y;
@@ -179,6 +181,7 @@ __global__ __launch_bounds__(kBlock) void k_scatter(const int32_t* __restrict__ 
     const int32_t* lab = labels + b * N;
     int32_t* cur = cursor + b * K;
     int32_t* out = sorted_idx + b * N;
+    int32_t* olab = sorted_lab ? sorted_lab + b * N : nullptr;
     if (use_lds) {
         for (int64_t k = threadIdx.x; k < K; k += kBlock) s_base[k] = 0;
         __syncthreads();
@@ -195,77 +198,92 @@ __global__ __launch_bounds__(kBlock) void k_scatter(const int32_t* __restrict__ 
         __syncthreads();
         for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
             const int32_t a = lab[i];
-            if (a >= 0 && a < K) out[atomicAdd(&s_base[a], 1)] = (int32_t)i;
+            if (a >= 0 && a < K) {
+                const int32_t pos = atomicAdd(&s_base[a], 1);
+                out[pos] = (int32_t)i;
+                if (olab) olab[pos] = a;
+            }
         }
     } else {
         for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
             const int32_t a = lab[i];
-            if (a >= 0 && a < K) out[atomicAdd(&cur[a], 1)] = (int32_t)i;
+            if (a >= 0 && a < K) {
+                const int32_t pos = atomicAdd(&cur[a], 1);
+                out[pos] = (int32_t)i;
+                if (olab) olab[pos] = a;
+            }
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Loads the EPL elements of row `row` owned by this lane (dims e0..e0+EPL-1)
-// as fp32; dims at or beyond d read as zero.
+// The EPL stored elements of row `row` owned by this lane (dims e0..e0+EPL-1);
+// dims at or beyond d read as zero.
+template <typename T, int EPL>
+struct RowPart {
+    T v[EPL];
+};
 template <typename T, int EPL, bool VEC>
-__device__ inline void load_row_part(const T* __restrict__ base, int64_t row, int d, int e0,
-                                     float (&v)[EPL]) {
+__device__ inline RowPart<T, EPL> load_row_part(const T* __restrict__ base, int64_t row, int d,
+                                                int e0) {
     const T* p = base + row * (int64_t)d + e0;
+    RowPart<T, EPL> r;
     if constexpr (VEC) {
-        T tmp[EPL];
-        __builtin_memcpy(tmp, __builtin_assume_aligned(p, EPL * sizeof(T) >= 16 ? 16 : EPL * sizeof(T)),
-                         sizeof(tmp));
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) v[e] = to_f32(tmp[e]);
+        __builtin_memcpy(r.v, __builtin_assume_aligned(p, EPL * sizeof(T) >= 16 ? 16 : EPL * sizeof(T)),
+                         sizeof(r.v));
     } else {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) v[e] = (e0 + e < d) ? to_f32(p[e]) : 0.f;
+        for (int e = 0; e < EPL; ++e) r.v[e] = (e0 + e < d) ? p[e] : (T)0;
     }
+    return r;
 }
 
-// Each wave reduces kSegChunk consecutive sorted positions.  sums must be zero
-// on entry (or hold earlier partial sums to accumulate into).
+// Rows gathered per batch so that the loaded values fit in about 64 VGPRs.
+template <typename T, int EPL>
+constexpr int seg_batch() {
+    constexpr int regs = (EPL * (int)sizeof(T) + 3) / 4;
+    return regs >= 64 ? 1 : 64 / regs;
+}
+
+// Each wave reduces kSegChunk = 64 consecutive sorted positions.  Its 64
+// point indices and labels arrive with one coalesced load (one per lane);
+// row addresses are then read lane by lane (readlane, no memory latency),
+// a batch of rows is loaded back to back, and the rows are added in order,
+// closing a piece with one row of atomic adds whenever the label changes.
+// sums must be zero on entry (or hold earlier partial sums to add to).
 template <typename T, int EPL, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_segment_sums(const T* __restrict__ X,
                                                          const int32_t* __restrict__ sorted_idx,
+                                                         const int32_t* __restrict__ sorted_lab,
                                                          const int32_t* __restrict__ offsets,
                                                          float* __restrict__ sums, int64_t N,
                                                          int64_t K, int d) {
+    static_assert(kSegChunk == kWave, "one sorted position per lane");
+    constexpr int RB = seg_batch<T, EPL>();
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t b = blockIdx.y;
-    const int32_t* __restrict__ off = offsets + b * (K + 1);
-    // positions past off[K] exist only when out-of-range labels were skipped
-    const int64_t total = off[K];
+    // positions past offsets[K] exist only when out-of-range labels were skipped
+    const int64_t total = offsets[b * (K + 1) + K];
     const int64_t p0 = ((int64_t)blockIdx.x * (kBlock / kWave) + wave) * kSegChunk;
     if (p0 >= total) return;
-    const int64_t p1 = min(p0 + (int64_t)kSegChunk, total);
-    const int32_t* __restrict__ sidx = sorted_idx + b * N;
+    const int n = (int)min((int64_t)kSegChunk, total - p0);  // positions of this wave
     const T* __restrict__ Xb = X + b * N * d;
     float* __restrict__ Sb = sums + b * K * d;
-
-    // the segment holding p0: the largest k with off[k] <= p0 (off[0] = 0 <= p0 < off[K])
-    int64_t lo = 0, hi = K;
-    while (hi - lo > 1) {
-        const int64_t mid = (lo + hi) >> 1;
-        if (off[mid] <= p0)
-            lo = mid;
-        else
-            hi = mid;
-    }
-    int64_t k = lo;
-    int64_t seg_end = off[k + 1];
+    const int64_t q = p0 + min(lane, n - 1);
+    const int32_t vidx = sorted_idx[b * N + q];
+    const int32_t vlab = sorted_lab[b * N + q];
 
     const int e0 = lane * EPL;
     const bool active = e0 < d;
     float acc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+    int32_t cur = __builtin_amdgcn_readfirstlane(vlab);
 
-    auto flush = [&](int64_t kk) {
+    auto flush = [&](int32_t kk) {
         if (active) {
-            float* dst = Sb + kk * d + e0;
+            float* dst = Sb + (int64_t)kk * d + e0;
 #pragma unroll
             for (int e = 0; e < EPL; ++e)
                 if (VEC || e0 + e < d) atomicAdd(dst + e, acc[e]);
@@ -274,35 +292,35 @@ __global__ __launch_bounds__(kBlock) void k_segment_sums(const T* __restrict__ X
         for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
     };
 
-    for (int64_t p = p0; p < p1; p += kSegUnroll) {
-        int32_t idx[kSegUnroll];
-        float v[kSegUnroll][EPL];
 #pragma unroll
-        for (int u = 0; u < kSegUnroll; ++u) idx[u] = (p + u < p1) ? sidx[p + u] : -1;
+    for (int base = 0; base < kSegChunk; base += RB) {
+        if (base < n) {
+            // all loads of the batch first, unconditionally, so they are in
+            // flight together: positions past n re-read the last row and
+            // lanes past d read the row start; neither is ever added
+            RowPart<T, EPL> v[RB];
 #pragma unroll
-        for (int u = 0; u < kSegUnroll; ++u) {
-            if (idx[u] >= 0 && active)
-                load_row_part<T, EPL, VEC>(Xb, idx[u], d, e0, v[u]);
-            else
+            for (int u = 0; u < RB; ++u) {
+                const int32_t row = __builtin_amdgcn_readlane(vidx, base + u);
+                v[u] = load_row_part<T, EPL, VEC>(Xb, row, d, active ? e0 : 0);
+            }
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) v[u][e] = 0.f;
-        }
+            for (int u = 0; u < RB; ++u) {
+                if (base + u < n) {
+                    const int32_t a = __builtin_amdgcn_readlane(vlab, base + u);
+                    if (a != cur) {
+                        flush(cur);
+                        cur = a;
+                    }
+                    if (active) {
 #pragma unroll
-        for (int u = 0; u < kSegUnroll; ++u) {
-            if (p + u < p1) {
-                if (p + u >= seg_end) {
-                    flush(k);
-                    do {
-                        ++k;
-                        seg_end = off[k + 1];
-                    } while (seg_end <= p + u);
+                        for (int e = 0; e < EPL; ++e) acc[e] += to_f32(v[u].v[e]);
+                    }
                 }
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) acc[e] += v[u][e];
             }
         }
     }
-    flush(k);
+    flush(cur);
 }
 
 // ---------------------------------------------------------------------------
@@ -351,8 +369,9 @@ inline unsigned grid_rows(int64_t rows) {
 }
 
 template <typename T>
-hipError_t segment_sums_t(const void* X, const int32_t* sorted_idx, const int32_t* offsets,
-                          float* sums, int64_t B, int64_t N, int64_t K, int d, hipStream_t s) {
+hipError_t segment_sums_t(const void* X, const int32_t* sorted_idx, const int32_t* sorted_lab,
+                          const int32_t* offsets, float* sums, int64_t B, int64_t N, int64_t K,
+                          int d, hipStream_t s) {
     const int epl = (d + kWave - 1) / kWave;
     const dim3 grid((unsigned)((N + (int64_t)kSegChunk * (kBlock / kWave) - 1) /
                                ((int64_t)kSegChunk * (kBlock / kWave))),
@@ -362,10 +381,10 @@ hipError_t segment_sums_t(const void* X, const int32_t* sorted_idx, const int32_
     if (epl <= E) {                                                                           \
         if (d % E == 0)                                                                       \
             hipLaunchKernelGGL((k_segment_sums<T, E, true>), grid, dim3(kBlock), 0, s, x,     \
-                               sorted_idx, offsets, sums, N, K, d);                           \
+                               sorted_idx, sorted_lab, offsets, sums, N, K, d);               \
         else                                                                                  \
             hipLaunchKernelGGL((k_segment_sums<T, E, false>), grid, dim3(kBlock), 0, s, x,    \
-                               sorted_idx, offsets, sums, N, K, d);                           \
+                               sorted_idx, sorted_lab, offsets, sums, N, K, d);               \
         return hipGetLastError();                                                             \
     }
     FK_SEG_CASE(1)
@@ -444,23 +463,26 @@ hipError_t launch_scan(const int32_t* counts, int32_t* offsets, int32_t* cursor,
     return hipGetLastError();
 }
 
-hipError_t launch_scatter(const int32_t* labels, int32_t* cursor, int32_t* sorted_idx, int64_t B,
-                          int64_t N, int64_t K, hipStream_t s) {
+hipError_t launch_scatter(const int32_t* labels, int32_t* cursor, int32_t* sorted_idx,
+                          int32_t* sorted_lab, int64_t B, int64_t N, int64_t K, hipStream_t s) {
     const int use_lds = K <= kLdsBinsMax;
     const size_t lds = use_lds ? (size_t)K * sizeof(int32_t) : 0;
     const dim3 grid((unsigned)((N + kSortTile - 1) / kSortTile), (unsigned)B);
-    hipLaunchKernelGGL(k_scatter, grid, dim3(kBlock), lds, s, labels, cursor, sorted_idx, N, K,
-                       use_lds);
+    hipLaunchKernelGGL(k_scatter, grid, dim3(kBlock), lds, s, labels, cursor, sorted_idx,
+                       sorted_lab, N, K, use_lds);
     return hipGetLastError();
 }
 
 hipError_t launch_segment_sums(int dtype, const void* X, const int32_t* sorted_idx,
-                               const int32_t* offsets, float* sums, int64_t B, int64_t N,
-                               int64_t K, int d, hipStream_t s) {
+                               const int32_t* sorted_lab, const int32_t* offsets, float* sums,
+                               int64_t B, int64_t N, int64_t K, int d, hipStream_t s) {
     switch (dtype) {
-        case FK_F32: return segment_sums_t<float>(X, sorted_idx, offsets, sums, B, N, K, d, s);
-        case FK_F16: return segment_sums_t<_Float16>(X, sorted_idx, offsets, sums, B, N, K, d, s);
-        default: return segment_sums_t<__bf16>(X, sorted_idx, offsets, sums, B, N, K, d, s);
+        case FK_F32:
+            return segment_sums_t<float>(X, sorted_idx, sorted_lab, offsets, sums, B, N, K, d, s);
+        case FK_F16:
+            return segment_sums_t<_Float16>(X, sorted_idx, sorted_lab, offsets, sums, B, N, K, d, s);
+        default:
+            return segment_sums_t<__bf16>(X, sorted_idx, sorted_lab, offsets, sums, B, N, K, d, s);
     }
 }
 
