@@ -18,6 +18,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -66,8 +67,13 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run plain 1 GiB device copies (PMC byte-counter calibration)")
+                    help="also run a plain 1 GiB -> 1 GiB copy kernel (PMC byte-counter calibration)")
+    ap.add_argument("--summarize", nargs="+", metavar="ARG",
+                    help="no GPU work: 'stats CSV CMD' prints a kernel-time summary; "
+                         "'traffic FETCH_CSV WRITE_CSV WORKLOAD CMD' writes the assign traffic record")
     args = ap.parse_args()
+    if args.summarize:
+        return summarize(args.summarize)
 
     if args.gpus != 1:
         msg = ("this build runs on one GPU only: pass --gpus 1 (the problems of a batch are "
@@ -134,10 +140,12 @@ def main() -> int:
     log(f"[bench] {args.steps} steps: {total_ms:.3f} ms (events), {wall * 1e3:.3f} ms (wall)")
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        # an elementwise kernel (a same-dtype copy_ would be a DMA memcpy, which
+        # the per-dispatch counters do not see): reads 1 GiB, writes 1 GiB
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
@@ -248,6 +256,64 @@ def run_cpu_baseline(w, X_cpu, Cq, fmt, target_s, gpu_value):
                    f"{t_assign:.1f} s assign + {t_update:.2f} s update per iteration"),
         "gpu_over_cpu": round(gpu_value / it_s, 1),
     }
+
+
+def _short_name(name: str) -> str:
+    """Kernel name without template arguments or parameter lists."""
+    m = re.search(r"(k_[a-z0-9_]+)", name)
+    if m and "fk" in name:
+        return m.group(1)
+    return re.sub(r"\(.*", "", name)[:60]
+
+
+def summarize(argv) -> int:
+    """Turn rocprofv3 CSV output into the short text summaries kept with the
+    sources: 'stats' (kernel-trace --stats) or 'traffic' (two --pmc runs)."""
+    import csv
+
+    kind = argv[0]
+    if kind == "stats":
+        path, cmd = argv[1], " ".join(argv[2:])
+        rows = list(csv.DictReader(open(path)))
+        print(f"# rocprofv3 kernel statistics\n\ncommand: `{cmd}`\n")
+        print("| kernel | calls | avg us | min us | max us | % of GPU time |")
+        print("|---|---|---|---|---|---|")
+        for r in rows:
+            print(f"| {_short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                  f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                  f"{float(r['Percentage']):.2f} |")
+        return 0
+    if kind == "traffic":
+        fetch_csv, write_csv, workload, cmd = argv[1], argv[2], argv[3], " ".join(argv[4:])
+
+        def per_dispatch(path, counter):
+            """{kernel: [KiB per dispatch]} for one counter."""
+            out = {}
+            for r in csv.DictReader(open(path)):
+                if r["Counter_Name"] != counter:
+                    continue
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+            return out
+
+        res = {}
+        for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+            d = per_dispatch(path, counter)
+            assign = [v for k, vs in d.items() if "k_assign" in k for v in vs]
+            copy = [v for k, vs in d.items() if "elementwise" in k and "Mul" in k for v in vs]
+            copy = [v for v in copy if v > 0.5 * max(copy)]   # the 1 GiB copies only
+            kib_copy = sum(copy) / len(copy)
+            factor = (1 << 20) / kib_copy        # true KiB of a 1 GiB stream / counted KiB
+            res[counter] = {"assign_kib_per_dispatch": sum(assign) / len(assign),
+                            "assign_dispatches": len(assign),
+                            "copy_1GiB_counted_kib": kib_copy, "calibration_factor": factor}
+        hbm = sum(r["assign_kib_per_dispatch"] * 1024 * r["calibration_factor"] for r in res.values())
+        rec = {"workload": workload, "kernel": "k_assign", "command": cmd,
+               "counters": res, "hbm_bytes_per_launch": round(hbm),
+               "assign_sources_sha256_16": assign_sources_hash()}
+        print(json.dumps(rec, indent=1))
+        return 0
+    log(f"unknown summary kind {kind!r}")
+    return 2
 
 
 if __name__ == "__main__":

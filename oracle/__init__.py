@@ -8,7 +8,7 @@ The arithmetic lives in ``oracle.c`` (plain C, fp64, OpenMP over points); this
 module only marshals numpy arrays.  What each function computes, and which
 passage of the pages it follows, is stated in ``oracle.c``.
 
-Conventions (readings of the pages, listed in the design doc):
+Conventions (readings where the pages are silent):
   * labels are 0-based int32; the lowest index wins an exact tie;
   * an empty cluster keeps its previous centroid;
   * counts are exact integers.

@@ -45,9 +45,10 @@ class Workload:
     init_seed: int
 
 
-# The five workloads (sizes, distributions, iteration counts) of the headline
-# benchmark definition.  Readings where the definition is silent are listed in
-# DESIGN.md ("Input recipe").
+# The five workloads (sizes, distributions, iteration counts).  Where a
+# workload's definition leaves a value open (the noise level and init of the
+# last three, the per-coordinate noise of the unit-vector one) the value here
+# is a reading: the one the other workloads use.
 CONFIGS = {
     1: Workload("gmm32_n4096_k32_d128_f32", 1, 4096, 32, 128, "f32", 10, 2.0, 1.0,
                 "equal-exact", False, "first", 1001, 2001),
