@@ -22,8 +22,8 @@
 //    permutation is applied to the centroid operand, so the dot product is
 //    unchanged and each lane reads one contiguous half row.
 //  * X rows of a wave stay in VGPRs for the whole K loop; centroid tiles of
-//    32 rows stream HBM/L2 -> registers -> LDS, double buffered, one barrier
-//    per tile.
+//    32 rows stream HBM/L2 -> registers -> a ring of three LDS buffers, one
+//    barrier per tile.
 //  * Exact tie rule: within a lane rows are visited in ascending index and a
 //    row replaces the best only when strictly larger; half-waves merge
 //    lexicographically on (score, index).  Padded centroid rows carry a
@@ -93,27 +93,16 @@ struct Mfma<float> {
     }
 };
 
-constexpr int kAssignBK = 32;  // centroids per tile (one MFMA row block)
+
+constexpr int kAssignBK = 32;    // centroids per tile (one MFMA row block)
 constexpr int kAssignWaves = 8;  // two waves per SIMD, one workgroup per CU
+constexpr int kAssignRing = 4;   // centroid tiles resident in LDS at once
 constexpr int kLdsBytes = 160 * 1024;
 
-// LDS of a workgroup: optionally the X block of the next item (points x
-// padded row), two centroid tiles (rows padded by 16 bytes) and their bias.
-constexpr int assign_lds(int Q, int NB, bool prefx) {
-    return (prefx ? kAssignWaves * NB * 32 * 2 * Q * 16 : 0) + 2 * kAssignBK * (2 * Q * 16 + 16) +
-           2 * kAssignBK * 4;
-}
-// Prefetching the next item's X block through LDS (persistent workgroups)
-// measured no faster on MI355X than loading X at the item start, so it is
-// off; the path stays for experiments with other shapes.
-constexpr bool assign_prefetch_x(int Q, int NB) {
-    return false && assign_lds(Q, NB, true) <= kLdsBytes;
-}
-// Staging register sets for centroid tiles: four (loads two iterations
-// ahead of their LDS store) when a thread moves at most two chunks per
-// tile, else two (one iteration ahead).
-constexpr int assign_sets(int Q) {
-    return (kAssignBK * 2 * Q + kAssignWaves * kWave - 1) / (kAssignWaves * kWave) <= 2 ? 4 : 2;
+// LDS of a workgroup: a ring of centroid tiles (rows padded by 16 bytes so
+// the fragment reads are bank-conflict free) and their bias values.
+constexpr int assign_lds(int Q) {
+    return kAssignRing * (kAssignBK * (2 * Q * 16 + 16) + kAssignBK * 4);
 }
 
 // Loads 16 bytes (V elements) of row `row` starting at element e0; elements
@@ -145,27 +134,32 @@ __device__ inline u32x4 load_chunk(const T* __restrict__ base, int64_t row, int6
 //   one; seeing a centroid twice cannot change a strict-">" running argmax
 //   (same score, later in the scan), so no padding is needed.
 //
-// An item is a block of 8*NB*32 points of one problem.  With PREFX the
-// kernel is persistent (one workgroup per CU walks the items) and, while it
-// runs the K loop of an item, prefetches the X block of its next item into
-// LDS, one 16-byte chunk per thread per tile iteration; the block is copied
-// into registers at the item switch, so no wave waits for X from memory.
-// Without PREFX (rows too long for the LDS budget) each workgroup takes one
-// item and loads its X straight into registers.
+// A workgroup takes one item (8*NB*32 points of one problem) and loads the
+// X fragments of its points straight into registers, where they stay for
+// the whole K loop.
 //
-// Pipeline per wave and item: the MFMAs of tile t+1 are issued interleaved
-// with the compare / select epilogue of tile t (sched_group_barrier); the
-// centroid tiles reach LDS through NSET staging register sets, loaded D
-// tiles ahead of use; one barrier per tile.
+// Pipeline per wave (iteration t computes the MFMAs of tile t+1 and the
+// epilogue of tile t):
+//   * centroid tiles move HBM/L2 -> two register staging sets -> a ring of
+//     four LDS buffers (tile j in buffer j mod 4, so with the loop unrolled
+//     four times every LDS address is a constant offset): tile t+4 is loaded
+//     in iteration t and stored to LDS at the end of iteration t+1;
+//   * the centroid fragments and bias of tile t+2 are read from LDS during
+//     iteration t, right after the MFMA that frees their registers, so the
+//     reads of all waves spread over a whole tile instead of queueing behind
+//     the barrier;
+//   * the MFMAs of tile t+1 go out slot by slot (a slot = the NB MFMAs
+//     sharing one centroid fragment and k-step) and each slot is preceded by
+//     a slice of tile t's compare / select epilogue; scheduling barriers pin
+//     that order, so each MFMA runs on the matrix unit while the wave's next
+//     slice runs on the vector unit;
+//   * one barrier per tile.
 template <typename T, int Q, int NB, bool VEC, bool EXACT, bool SMALLK>
 __global__ __launch_bounds__(kAssignWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __restrict__ bias,
               int32_t* __restrict__ labels, float* __restrict__ min_dist, int64_t B, int64_t N,
               int64_t K, int d) {
     using M = Mfma<T>;
-    constexpr bool PREFX = assign_prefetch_x(Q, NB);
-    constexpr int NSET = assign_sets(Q);
-    constexpr int D = NSET == 2 ? 3 : 4;               // load tile t+D in iteration t
     constexpr int V = 16 / sizeof(T);
     constexpr int HR = Q * V;                          // dimensions per half row
     constexpr int RC = 2 * Q;                          // 16-byte chunks per padded row
@@ -175,16 +169,17 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
     constexpr int NT = kAssignWaves * kWave;
     constexpr int PER = (CHUNKS + NT - 1) / NT;
     constexpr int PTS = kAssignWaves * NB * 32;        // points per item
-    constexpr int XPT = PTS * RC / NT;                 // X chunks per thread per item
-    constexpr int XB = PREFX ? PTS * RC * 16 : 0;      // LDS bytes of the X buffer
+    constexpr int kSlots = Q * M::kSteps;
+    // fragments of the next tile prefetched during an iteration, and the slot
+    // after which the next tile's bias is read (late, to keep it out of the
+    // registers for most of the iteration)
+    constexpr int P = Q <= 4 ? Q : 4;
+    constexpr int kBiasSlot = kSlots > 3 ? kSlots - 3 : 0;
     static_assert(!EXACT || VEC, "EXACT implies VEC");
-    static_assert((PTS * RC) % NT == 0, "X chunks divide evenly");
-    static_assert(D != 2 + NSET && (D - 2) % NSET != 0, "load and store sets differ");
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    char* s_x = smem;                                               // [PTS][RC] swizzled
-    char* s_tile = smem + XB;                                       // [2][TILEB]
-    float* s_bias = reinterpret_cast<float*>(s_tile + 2 * TILEB);   // [2][BK]
+    char* s_tile = smem;                                                      // [ring][TILEB]
+    float* s_bias = reinterpret_cast<float*>(smem + kAssignRing * TILEB);     // [ring][BK]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -196,30 +191,6 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
     const int lastbase = SMALLK ? 0 : K32 - kAssignBK;
     const int64_t nbpp = (N + PTS - 1) / PTS;          // items per problem
     const int64_t items = B * nbpp;
-
-    // ---- X block staging: chunk c of thread tid is point p, logical chunk
-    // lc of that point; LDS slot p*RC + (lc ^ (p % RC)) (conflict-free reads)
-    const int N32 = (int)N;
-    // chunk c of this thread for the item whose X rows start at Xi and whose
-    // first point is row r0 of its problem
-    auto x_load = [&](const T* Xi, int r0, int c) -> u32x4 {
-        const int g = c * NT + tid;
-        const int p = g / RC;
-        const int lc = g % RC;
-        const int row = min(r0 + p, N32 - 1);  // rows past N: any finite data
-        if constexpr (VEC) {
-            const int e0 = EXACT ? lc * V : min(lc * V, d - V);  // zeroed after the copy
-            return *reinterpret_cast<const u32x4*>(Xi + (int64_t)row * d + e0);
-        } else {
-            return load_chunk<T, false>(Xi, row, N, d, lc * V);
-        }
-    };
-    auto x_store = [&](int c, u32x4 v) {
-        const int g = c * NT + tid;
-        const int p = g / RC;
-        const int lc = g % RC;
-        *reinterpret_cast<u32x4*>(s_x + (p * RC + (lc ^ (p & (RC - 1)))) * 16) = v;
-    };
 
     // ---- centroid tile staging (registers -> LDS).  Thread tid always moves
     // the same (row, chunk) pairs of a tile, so each load is a uniform tile
@@ -241,7 +212,6 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
     struct Staged {
         u32x4 v[PER];
         float bias;
-        u32x4 x;  // one chunk of the next item's X block (PREFX)
     };
 
     float best[NB];
@@ -249,21 +219,7 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
     u32x4 xf[NB][Q];
     float xsq[NB];
 
-    int64_t item = blockIdx.x;
-    if (item >= items) return;
-    if constexpr (PREFX) {  // first item: its X block straight into LDS
-        const int64_t b0 = item / nbpp;
-        const T* Xi = X + b0 * N * d;
-        const int r0 = (int)(item - b0 * nbpp) * PTS;
-        for (int c = 0; c < XPT; ++c) x_store(c, x_load(Xi, r0, c));
-        __syncthreads();
-    }
-
-    for (; item < items; item += gridDim.x) {
-        const int64_t next = PREFX && item + gridDim.x < items ? item + gridDim.x : item;
-        const int64_t bn = next / nbpp;
-        const T* Xn = X + bn * N * d;                  // next item's problem
-        const int rn = (int)(next - bn * nbpp) * PTS;  // next item's first point
+    for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
         const int64_t b = item / nbpp;
         const int64_t pbase = (item - b * nbpp) * PTS + (int64_t)wave * NB * 32;
         const T* __restrict__ Cb = C + b * K * d;
@@ -272,20 +228,10 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
         // ---- this item's points, resident in registers for the K loop
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const int p = wave * NB * 32 + nb * 32 + col;
 #pragma unroll
-            for (int q = 0; q < Q; ++q) {
-                u32x4 v;
-                if constexpr (PREFX) {
-                    const int lc = h * Q + q;
-                    v = *reinterpret_cast<const u32x4*>(s_x + (p * RC + (lc ^ (p & (RC - 1)))) * 16);
-                    if (!EXACT && h * HR + q * V >= d) v = (u32x4){0u, 0u, 0u, 0u};
-                } else {
-                    v = load_chunk<T, VEC>(X + b * N * d, pbase + nb * 32 + col, N, d,
-                                           h * HR + q * V);
-                }
-                xf[nb][q] = v;
-            }
+            for (int q = 0; q < Q; ++q)
+                xf[nb][q] = load_chunk<T, VEC>(X + b * N * d, pbase + nb * 32 + col, N, d,
+                                               h * HR + q * V);
             xsq[nb] = 0.f;
             best[nb] = -INFINITY;
             bidx[nb] = 0;
@@ -296,7 +242,6 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
 #pragma unroll
                 for (int q = 0; q < Q; ++q) xsq[nb] += M::sumsq(xf[nb][q]);
         }
-        if constexpr (PREFX) __syncthreads();  // the X buffer may now receive the next item
 
         auto gload = [&](int t, Staged& st) {
             const int tbase = tile_base(t);
@@ -318,11 +263,8 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
             } else {
                 st.bias = biasb[tbase + (tid & (kAssignBK - 1))];
             }
-            // X chunk t-D of the next item rides along with tile t (chunks
-            // before 0 and past XPT-1 repeat the first / last one)
-            if constexpr (PREFX) st.x = x_load(Xn, rn, min(max(t - D, 0), XPT - 1));
         };
-        auto sstore = [&](int buf, const Staged& st, int t) {
+        auto sstore = [&](int buf, const Staged& st) {
 #pragma unroll
             for (int u = 0; u < PER; ++u)
                 if (CHUNKS % NT == 0 || u * NT + tid < CHUNKS)
@@ -331,12 +273,14 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
             // every thread stores its bias value (identical stores per slot),
             // so the loop body has no branch
             s_bias[buf * kAssignBK + (tid & (kAssignBK - 1))] = st.bias;
-            if constexpr (PREFX) x_store(min(max(t - D, 0), XPT - 1), st.x);
         };
-
-        // MFMAs of the tile in LDS buffer `buf`; the accumulators start at
-        // the bias of their rows (8g + 4h + i, g, i = 0..3).
-        auto mma = [&](int buf, floatx16 (&acc)[NB]) {
+        // this lane's centroid fragment q of the tile in LDS buffer buf
+        auto frag = [&](int buf, int q) -> u32x4 {
+            return *reinterpret_cast<const u32x4*>(s_tile + buf * TILEB + col * ROWB +
+                                                   (h * Q + q) * 16);
+        };
+        // bias of this lane's accumulator rows 8g + 4h + i (g, i = 0..3)
+        auto bias_vec = [&](int buf) -> floatx16 {
             floatx16 bv;
             const float* sb = s_bias + buf * kAssignBK + 4 * h;
 #pragma unroll
@@ -347,45 +291,38 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
                 bv[4 * g + 2] = v4[2];
                 bv[4 * g + 3] = v4[3];
             }
-            const char* arow = s_tile + buf * TILEB + col * ROWB + h * Q * 16;
-#pragma unroll
-            for (int q = 0; q < Q; ++q) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(arow + q * 16);
-#pragma unroll
-                for (int e = 0; e < M::kSteps; ++e) {
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        acc[nb] = M::step(a, xf[nb][q], (q == 0 && e == 0) ? bv : acc[nb], e);
-                }
-            }
+            return bv;
         };
 
-        // Running (max score, lowest index).  Within a tile the candidate
-        // index is the lane's row offset 8*(r/4) + r%4 (a small inline
-        // constant, -1 = no improvement in this tile); rows ascend with r, so
-        // strict > keeps the lowest index.  The tile base is added once per
-        // tile.  The NB chains are independent; interleaving them spaces each
-        // compare from the select that consumes it.
-        auto epilogue = [&](const floatx16 (&acc)[NB], int t) {
-            const int32_t kb = tile_base(t);
-            float m[NB];
-            int32_t rt[NB];
+        // Running (max score, lowest index) over the rows of one tile's
+        // scores.  Within a tile the candidate index is the lane's row offset
+        // 8*(r/4) + r%4 (a small inline constant, -1 = no improvement in this
+        // tile); rows ascend with r, so strict > keeps the lowest index.  The
+        // tile base is added once per tile.
+        float m[NB];
+        int32_t rt[NB];
+        auto epi_begin = [&]() {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 m[nb] = best[nb];
                 rt[nb] = -1;
             }
+        };
+        auto epi_rows = [&](const floatx16(&sc)[NB], int r0, int r1) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            for (int r = r0; r < r1; ++r) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    const float s = acc[nb][r];
+                    const float s = sc[nb][r];
                     // written as "keep" so both selects take the 2-operand form
                     const bool keep = !(s > m[nb]);
                     m[nb] = keep ? m[nb] : s;
                     rt[nb] = keep ? rt[nb] : 8 * (r >> 2) + (r & 3);
                 }
             }
+        };
+        auto epi_end = [&](int t) {
+            const int32_t kb = tile_base(t);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 best[nb] = m[nb];
@@ -394,70 +331,105 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
         };
 
         floatx16 acc[2][NB];
-        Staged st[NSET];
-        constexpr int U = NSET == 4 ? 4 : 2;  // unroll: acc parity and set rotation repeat
-        // set holding tile j: st[j % NSET]; with two sets tile 2 reuses tile
-        // 0's set once tile 0 is in LDS
-#pragma unroll
-        for (int j = 0; j < (D < NSET ? D : NSET); ++j) gload(j, st[j]);
-        sstore(0, st[0], 0);
-#pragma unroll
-        for (int j = NSET; j < D; ++j) gload(j, st[j % NSET]);
-        __syncthreads();
-        mma(0, acc[0]);
-        sstore(1, st[1 % NSET], 1);
-        __syncthreads();
+        Staged st[2];
+        u32x4 a[Q];    // centroid fragments of the tile whose MFMAs run next
+        floatx16 bv;   // and its bias
 
-        // iteration t (t + 1 < ntiles): tile t's scores are in acc[t&1],
-        // tile t+1 is in LDS buffer (t+1)&1, tile t+2 waits in its set and
-        // tile t+D is loaded.  The body is one basic block; the schedule
-        // interleaves every MFMA of tile t+1 with a few epilogue instructions
-        // of tile t, so the vector unit works while the matrix unit runs.
-        auto iteration = [&](int t, int i) {
-            gload(t + D, st[(i + D) % NSET]);
-            mma((i + 1) & 1, acc[(i + 1) & 1]);
-            epilogue(acc[i & 1], t);
-            sstore(i & 1, st[(i + 2) % NSET], t + 2);
-            constexpr int kMfma = NB * Q * M::kSteps;
-            constexpr int kValuPer = (NB * 48 + kMfma - 1) / kMfma + 1;
-            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);                       // bias + A reads
-            __builtin_amdgcn_sched_group_barrier(0x020, PER + 1 + (PREFX ? 1 : 0), 0);  // loads
+        // ---- prologue: tiles 0, 1, 2 into LDS, tile 3 staged; tile 0's
+        // MFMAs; tile 1's first fragments and bias prefetched
+        gload(0, st[0]);
+        gload(1, st[1]);
+        sstore(0, st[0]);
+        sstore(1, st[1]);
+        gload(2, st[0]);
+        gload(3, st[1]);
+        sstore(2, st[0]);
+        __syncthreads();
+        bv = bias_vec(0);
 #pragma unroll
-            for (int k = 0; k < kMfma; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);  // epilogue VALU
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // next A read
+        for (int q = 0; q < Q; ++q) {
+            const u32x4 f = frag(0, q);
+#pragma unroll
+            for (int e = 0; e < M::kSteps; ++e)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[0][nb] = M::step(f, xf[nb][q], (q == 0 && e == 0) ? bv : acc[0][nb], e);
+        }
+#pragma unroll
+        for (int q = 0; q < P; ++q) a[q] = frag(1, q);
+        bv = bias_vec(1);
+
+        // ---- iteration t (t + 1 < ntiles), i = t mod 4.  On entry
+        // acc[t mod 2] holds tile t's scores, a[0..P) and bv tile t+1's first
+        // fragments and bias; LDS holds tiles t+1 and t+2; staging set
+        // (t+1) mod 2 holds tile t+3.
+        auto iteration = [&](int t, int i) {
+            floatx16(&cur)[NB] = acc[(i & 1) ^ 1];
+            const floatx16(&prv)[NB] = acc[i & 1];
+            const int b1 = (i + 1) % kAssignRing;  // tile t+1
+            const int b2 = (i + 2) % kAssignRing;  // tile t+2
+            const int b3 = (i + 3) % kAssignRing;  // receives tile t+3
+            gload(t + 4, st[i & 1]);
+            u32x4 nx[P];
+            floatx16 nbv;
+            __builtin_amdgcn_sched_barrier(0);
+            epi_begin();
+#pragma unroll
+            for (int sl = 0; sl < kSlots; ++sl) {
+                const int q = sl / M::kSteps;
+                const int e = sl % M::kSteps;
+                epi_rows(prv, 16 * sl / kSlots, 16 * (sl + 1) / kSlots);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    cur[nb] = M::step(a[q], xf[nb][q], sl == 0 ? bv : cur[nb], e);
+                if (e == M::kSteps - 1) {
+                    // a[q] is free: read the fragment needed P slots later
+                    const int v = q + P;
+                    if (v < Q)
+                        a[v] = frag(b1, v);
+                    else
+                        nx[v - Q] = frag(b2, v - Q);
+                }
+                if (sl == kBiasSlot) nbv = bias_vec(b2);
+                __builtin_amdgcn_sched_barrier(0);
             }
+            epi_end(t);
+#pragma unroll
+            for (int q = 0; q < P; ++q) a[q] = nx[q];
+            bv = nbv;
+            sstore(b3, st[(i & 1) ^ 1]);
             __syncthreads();
         };
+        auto final_epilogue = [&](int t, const floatx16(&sc)[NB]) {
+            epi_begin();
+            epi_rows(sc, 0, 16);
+            epi_end(t);
+        };
         int t = 0;
-        for (; t + U < ntiles; t += U) {
+        for (; t + 4 < ntiles; t += 4) {
 #pragma unroll
-            for (int i = 0; i < U; ++i) iteration(t + i, i);
+            for (int i = 0; i < 4; ++i) iteration(t + i, i);
         }
-        // the last 1..U tiles: one fewer iteration, then the final epilogue
+        // the last one to four tiles
         switch (ntiles - t) {
             case 1:
-                epilogue(acc[0], t);
+                final_epilogue(t, acc[0]);
                 break;
             case 2:
                 iteration(t, 0);
-                epilogue(acc[1], t + 1);
+                final_epilogue(t + 1, acc[1]);
                 break;
             case 3:
-                if constexpr (U >= 4) {
-                    iteration(t, 0);
-                    iteration(t + 1, 1);
-                    epilogue(acc[0], t + 2);
-                }
+                iteration(t, 0);
+                iteration(t + 1, 1);
+                final_epilogue(t + 2, acc[0]);
                 break;
             default:
-                if constexpr (U >= 4) {
-                    iteration(t, 0);
-                    iteration(t + 1, 1);
-                    iteration(t + 2, 2);
-                    epilogue(acc[1], t + 3);
-                }
+                iteration(t, 0);
+                iteration(t + 1, 1);
+                iteration(t + 2, 2);
+                final_epilogue(t + 3, acc[1]);
                 break;
         }
 
@@ -479,57 +451,28 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
                 if (min_dist) min_dist[b * N + j] = xx - 2.f * sc;
             }
         }
-
-        if constexpr (PREFX) {
-            // ---- complete the next item's X block.  Tile j carries X chunk
-            // j-D.  Iterations 0 .. ntiles-2 loaded tiles up to ntiles-2+D
-            // and stored tiles up to ntiles, so the chunks of tiles ntiles+1
-            // .. ntiles+D-2 still sit in their sets and chunks from ntiles-1
-            // on were never loaded.
-#pragma unroll
-            for (int j = 1; j <= D - 2; ++j) {
-                const int tj = ntiles + j;      // tile whose set holds the chunk
-                const int c = tj - D;
-                if (c >= 0 && c < XPT) {
-                    const int si = tj % NSET;
-                    u32x4 v = st[0].x;
-#pragma unroll
-                    for (int k = 1; k < NSET; ++k)
-                        if (si == k) v = st[k].x;
-                    x_store(c, v);
-                }
-            }
-            for (int c = max(ntiles - 1, 0); c < XPT; ++c) x_store(c, x_load(Xn, rn, c));
-            __syncthreads();
-        }
+        __syncthreads();  // the next item's prologue rewrites the ring
     }
 }
+
 
 template <typename T, int Q, int NB, bool VEC, bool EXACT, bool SMALLK>
 hipError_t launch_assign_t(const void* X, const void* C, const float* bias, int32_t* labels,
                            float* min_dist, int64_t B, int64_t N, int64_t K, int d,
                            hipStream_t s) {
-    constexpr bool prefx = assign_prefetch_x(Q, NB);
-    constexpr int lds = assign_lds(Q, NB, prefx);
+    constexpr int lds = assign_lds(Q);
     static_assert(lds <= kLdsBytes, "LDS budget");
     constexpr int PTS = kAssignWaves * NB * 32;
     auto kern = k_assign<T, Q, NB, VEC, EXACT, SMALLK>;
     static bool attr_set = false;  // one attribute call per instantiation and process
-    static int cus = 0;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
-        int dev = 0;
-        e = hipGetDevice(&dev);
-        if (e != hipSuccess) return e;
-        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int64_t items = B * ((N + PTS - 1) / PTS);
-    // persistent: one workgroup per CU; otherwise one workgroup per item
-    const int64_t grid = prefx ? (items < cus ? items : cus) : items;
+    // one workgroup per item
+    const int64_t grid = B * ((N + PTS - 1) / PTS);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kAssignWaves * kWave), lds, s,
                        static_cast<const T*>(X), static_cast<const T*>(C), bias, labels, min_dist,
                        B, N, K, d);
@@ -566,7 +509,6 @@ hipError_t dispatch_assign(const void* X, const void* C, const float* bias, int3
     FK_ASSIGN_CASE(4, 2)
     FK_ASSIGN_CASE(8, 2)
     FK_ASSIGN_CASE(16, 1)
-    FK_ASSIGN_CASE(32, 1)
 #undef FK_ASSIGN_CASE
     return hipErrorInvalidValue;
 }

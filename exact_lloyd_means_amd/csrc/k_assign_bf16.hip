@@ -2,11 +2,11 @@
 #include "k_assign_splitd.inl"
 
 namespace fk {
-// Rows up to 512 dimensions keep each wave's points in registers for the
+// Rows up to 256 dimensions keep each wave's points in registers for the
 // whole K loop; longer rows stream d in chunks (split-d kernel).
 hipError_t launch_assign_bf16(const void* X, const void* C, const float* bias, int32_t* labels,
                          float* min_dist, int64_t B, int64_t N, int64_t K, int d, hipStream_t s) {
-    if (d > 512)
+    if (d > 256)
         return launch_assign_splitd<__bf16>(X, C, bias, labels, min_dist, B, N, K, d, s);
     return dispatch_assign<__bf16>(X, C, bias, labels, min_dist, B, N, K, d, s);
 }
