@@ -36,14 +36,19 @@ Workspace workspace_layout(const fk_problem& p, char* base) {
         return at;
     };
     const size_t B = (size_t)p.B, N = (size_t)p.N, K = (size_t)p.K, d = (size_t)p.d;
+    const size_t tab = (size_t)sort_table_bound(p.N, p.K);
     w.bias = reinterpret_cast<float*>(take(B * K * sizeof(float)));
     w.offsets = reinterpret_cast<int32_t*>(take(B * (K + 1) * sizeof(int32_t)));
-    w.cursor = reinterpret_cast<int32_t*>(take(B * K * sizeof(int32_t)));
+    w.table = reinterpret_cast<int32_t*>(take(B * tab * sizeof(int32_t)));
     w.sorted_idx = reinterpret_cast<int32_t*>(take(B * N * sizeof(int32_t)));
-    w.sorted_lab = reinterpret_cast<int32_t*>(take(B * N * sizeof(int32_t)));
+    w.poff = reinterpret_cast<int32_t*>(take(B * (K + 1) * sizeof(int32_t)));
+    w.pieces = reinterpret_cast<int32_t*>(
+        take(B * (1 + 2 * (size_t)piece_capacity(p.N, p.K)) * sizeof(int32_t)));
     w.sums = reinterpret_cast<float*>(take(B * K * d * sizeof(float)));
+    w.arrive = reinterpret_cast<int32_t*>(take(B * K * sizeof(int32_t)));
     w.counts = reinterpret_cast<int32_t*>(take(B * K * sizeof(int32_t)));
     w.lowp = p.dtype == FK_F32 ? nullptr : take(B * K * d * (size_t)dtype_size(p.dtype));
+    w.bad = reinterpret_cast<int32_t*>(take(B * sizeof(int32_t)));
     w.flags = reinterpret_cast<uint32_t*>(take(256));
     w.total = o;
     return w;
@@ -66,10 +71,12 @@ StreamWorkspace stream_workspace_layout(const fk_problem& p, int64_t chunk, char
     w.sums = reinterpret_cast<float*>(take(B * K * d * sizeof(float)));
     w.ccounts = reinterpret_cast<int32_t*>(take(K * sizeof(int32_t)));
     w.offsets = reinterpret_cast<int32_t*>(take((K + 1) * sizeof(int32_t)));
-    w.cursor = reinterpret_cast<int32_t*>(take(K * sizeof(int32_t)));
+    w.table = reinterpret_cast<int32_t*>(take((size_t)sort_table_bound(chunk, p.K) * sizeof(int32_t)));
     w.sorted_idx = reinterpret_cast<int32_t*>(take(c * sizeof(int32_t)));
-    w.sorted_lab = reinterpret_cast<int32_t*>(take(c * sizeof(int32_t)));
-    w.flags = reinterpret_cast<uint32_t*>(take(256));
+    w.poff = reinterpret_cast<int32_t*>(take((K + 1) * sizeof(int32_t)));
+    w.pieces = reinterpret_cast<int32_t*>(
+        take((1 + 2 * (size_t)piece_capacity(chunk, p.K)) * sizeof(int32_t)));
+    w.bad = reinterpret_cast<int32_t*>(take(256));
     w.total = o;
     return w;
 }
@@ -145,14 +152,29 @@ fk_status check_assign_d(const fk_problem&) { return FK_OK; }
         if (fk_s_ != FK_OK) return fk_s_; \
     } while (0)
 
-// Counting-sort argsort of the labels: counts, offsets, cursor, sorted_idx.
-fk_status enqueue_sort(const fk_problem& p, const int32_t* labels, int32_t* counts,
-                       int32_t* offsets, int32_t* cursor, int32_t* sorted_idx,
-                       int32_t* sorted_lab, uint32_t* flags, hipStream_t s) {
-    FK_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(counts), p.B * p.K, 0u, s), "clear counts");
-    FK_TRY(launch_histogram(labels, counts, flags, p.B, p.N, p.K, s), "histogram");
-    FK_TRY(launch_scan(counts, offsets, cursor, p.B, p.K, s), "scan");
-    FK_TRY(launch_scatter(labels, cursor, sorted_idx, sorted_lab, p.B, p.N, p.K, s), "scatter");
+// Counting-sort argsort of the labels into counts, offsets, sorted_idx and
+// the run labels of the segment sums; optionally clears the sums and arrival
+// counters of a fused update and the move word on the way.
+fk_status enqueue_sort(const fk_problem& p, const Workspace& w, const int32_t* labels,
+                       int32_t* counts, int32_t* offsets, int32_t* sorted_idx, bool clear_update,
+                       uint32_t* move, hipStream_t s) {
+    SortParams sp{};
+    sp.labels = labels;
+    sp.counts = counts;
+    sp.offsets = offsets;
+    sp.sorted_idx = sorted_idx;
+    sp.poff = w.poff;
+    sp.pieces = w.pieces;
+    sp.table = w.table;
+    sp.bad = w.bad;
+    sp.move = move;
+    if (clear_update) {
+        sp.zero[0] = reinterpret_cast<uint32_t*>(w.sums);
+        sp.zero_n[0] = p.B * p.K * p.d;
+        sp.zero[1] = reinterpret_cast<uint32_t*>(w.arrive);
+        sp.zero_n[1] = p.B * p.K;
+    }
+    FK_TRY(launch_sort(sp, p.B, p.N, p.K, s), "sort labels");
     return FK_OK;
 }
 
@@ -239,8 +261,7 @@ fk_status fk_sort_labels(const fk_problem* p, const int32_t* labels, int32_t* co
     Workspace w;
     FK_CHECK(check_ws(*p, ws, ws_bytes, &w));
     hipStream_t s = static_cast<hipStream_t>(stream);
-    FK_TRY(launch_fill_u32(w.flags, 64, 0u, s), "clear flags");
-    return enqueue_sort(*p, labels, counts, offsets, w.cursor, sorted_idx, nullptr, w.flags, s);
+    return enqueue_sort(*p, w, labels, counts, offsets, sorted_idx, false, nullptr, s);
 }
 
 fk_status fk_update(const fk_problem* p, const void* X, const int32_t* labels,
@@ -260,25 +281,16 @@ fk_status fk_update(const fk_problem* p, const void* X, const int32_t* labels,
     FK_CHECK(check_ws(*p, ws, ws_bytes, &w));
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t rows = p->B * p->K;
-    FK_TRY(launch_fill_u32(w.flags, 64, 0u, s), "clear flags");
-    FK_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(w.sums), rows * p->d, 0u, s), "clear sums");
-    FK_CHECK(enqueue_sort(*p, labels, counts, w.offsets, w.cursor, w.sorted_idx, w.sorted_lab,
-                          w.flags, s));
-    FK_TRY(launch_segment_sums(p->dtype, X, w.sorted_idx, w.sorted_lab, w.offsets, w.sums, p->B,
-                               p->N, p->K, (int)p->d, s),
+    FK_CHECK(enqueue_sort(*p, w, labels, counts, w.offsets, w.sorted_idx, true, nullptr, s));
+    SegParams sp{true, w.sums, w.arrive, C_prev, C_next,
+                 p->dtype == FK_F32 ? nullptr : C_next_lowp, nullptr, nullptr};
+    FK_TRY(launch_segment_sums(p->dtype, X, w.sorted_idx, w.offsets, w.pieces, sp, p->B, p->N,
+                               p->K, (int)p->d, s),
            "segment sums");
-    if (p->dtype == FK_F32 && C_next_lowp) {
-        FK_TRY(launch_finalize(p->dtype, w.sums, counts, C_prev, C_next, nullptr, nullptr, nullptr,
-                               rows, (int)p->d, s),
-               "finalize");
+    if (p->dtype == FK_F32 && C_next_lowp)
         FK_TRY(hipMemcpyAsync(C_next_lowp, C_next, (size_t)(rows * p->d) * sizeof(float),
                               hipMemcpyDeviceToDevice, s),
                "copy fp32 centroids");
-    } else {
-        FK_TRY(launch_finalize(p->dtype, w.sums, counts, C_prev, C_next, C_next_lowp, nullptr,
-                               nullptr, rows, (int)p->d, s),
-               "finalize");
-    }
     return FK_OK;
 }
 
@@ -301,22 +313,18 @@ fk_status fk_lloyd(const fk_problem* p, const void* X, float* C, int32_t* labels
     const bool sync = tol > 0.f || n_iter != nullptr;
     const void* Cq = p->dtype == FK_F32 ? static_cast<const void*>(C) : w.lowp;
 
-    FK_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(w.sums), rows * p->d, 0u, s), "clear sums");
     FK_TRY(launch_prepare(p->dtype, C, w.lowp, w.bias, rows, (int)p->d, s), "prepare centroids");
+    uint32_t* move = sync ? w.flags + 1 : nullptr;
+    const SegParams sp{true, w.sums, w.arrive, C, C, w.lowp, w.bias, move};
     int it = 0;
     while (it < max_iters) {
-        FK_TRY(launch_fill_u32(w.flags, 64, 0u, s), "clear flags");
         FK_TRY(launch_assign(p->dtype, X, Cq, w.bias, labels, nullptr, p->B, p->N, p->K,
                              (int)p->d, s),
                "assign");
-        FK_CHECK(enqueue_sort(*p, labels, counts, w.offsets, w.cursor, w.sorted_idx, w.sorted_lab,
-                              w.flags, s));
-        FK_TRY(launch_segment_sums(p->dtype, X, w.sorted_idx, w.sorted_lab, w.offsets, w.sums,
-                                   p->B, p->N, p->K, (int)p->d, s),
+        FK_CHECK(enqueue_sort(*p, w, labels, counts, w.offsets, w.sorted_idx, true, move, s));
+        FK_TRY(launch_segment_sums(p->dtype, X, w.sorted_idx, w.offsets, w.pieces, sp, p->B,
+                                   p->N, p->K, (int)p->d, s),
                "segment sums");
-        FK_TRY(launch_finalize(p->dtype, w.sums, counts, C, C, w.lowp, w.bias,
-                               sync ? w.flags + 1 : nullptr, rows, (int)p->d, s),
-               "finalize");
         ++it;
         if (sync) {
             uint32_t bits = 0;
@@ -379,7 +387,6 @@ fk_status fk_lloyd_streamed(const fk_problem* p, const void* X_host, int64_t chu
     }
     auto body = [&]() -> fk_status {
         const int dt = p->dtype;
-        FK_TRY(launch_fill_u32(w.flags, 64, 0u, cs), "clear flags");
         FK_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(w.sums), rows * d, 0u, cs), "clear sums");
         FK_TRY(launch_prepare(dt, C, w.lowp, w.bias, rows, (int)d, cs), "prepare centroids");
         const void* Cq = dt == FK_F32 ? static_cast<const void*>(C) : w.lowp;
@@ -404,13 +411,20 @@ fk_status fk_lloyd_streamed(const fk_problem* p, const void* X_host, int64_t chu
                     FK_TRY(launch_assign(dt, w.xbuf[buf], Cqb, w.bias + b * K, lab, nullptr, 1, n, K,
                                          (int)d, cs),
                            "assign");
-                    FK_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(w.ccounts), K, 0u, cs), "clear chunk counts");
-                    FK_TRY(launch_histogram(lab, w.ccounts, w.flags, 1, n, K, cs), "histogram");
-                    FK_TRY(launch_scan(w.ccounts, w.offsets, w.cursor, 1, K, cs), "scan");
-                    FK_TRY(launch_scatter(lab, w.cursor, w.sorted_idx, w.sorted_lab, 1, n, K, cs),
-                           "scatter");
-                    FK_TRY(launch_segment_sums(dt, w.xbuf[buf], w.sorted_idx, w.sorted_lab, w.offsets,
-                                               w.sums + b * K * d, 1, n, K, (int)d, cs),
+                    SortParams so{};
+                    so.labels = lab;
+                    so.counts = w.ccounts;
+                    so.offsets = w.offsets;
+                    so.sorted_idx = w.sorted_idx;
+                    so.poff = w.poff;
+                    so.pieces = w.pieces;
+                    so.table = w.table;
+                    so.bad = w.bad;
+                    FK_TRY(launch_sort(so, 1, n, K, cs), "sort chunk labels");
+                    const SegParams sp{false, w.sums + b * K * d, nullptr, nullptr, nullptr,
+                                       nullptr, nullptr, nullptr};
+                    FK_TRY(launch_segment_sums(dt, w.xbuf[buf], w.sorted_idx, w.offsets, w.pieces,
+                                               sp, 1, n, K, (int)d, cs),
                            "segment sums");
                     FK_TRY(launch_add_i32(counts + b * K, w.ccounts, K, cs), "add counts");
                     FK_TRY(hipEventRecord(done[buf], cs), "record done");
@@ -436,10 +450,17 @@ fk_status fk_error_count(const fk_problem* p, const void* ws, size_t ws_bytes, i
     Workspace w;
     FK_CHECK(check_ws(*p, const_cast<void*>(ws), ws_bytes, &w));
     hipStream_t s = static_cast<hipStream_t>(stream);
-    uint32_t v = 0;
-    FK_TRY(hipMemcpyAsync(&v, w.flags, sizeof(v), hipMemcpyDeviceToHost, s), "read error count");
-    FK_TRY(hipStreamSynchronize(s), "synchronise");
-    *count = v;
+    int64_t total = 0;
+    int32_t part[256];
+    for (int64_t b0 = 0; b0 < p->B; b0 += 256) {
+        const int64_t nb = p->B - b0 < 256 ? p->B - b0 : 256;
+        FK_TRY(hipMemcpyAsync(part, w.bad + b0, (size_t)nb * sizeof(int32_t),
+                              hipMemcpyDeviceToHost, s),
+               "read error count");
+        FK_TRY(hipStreamSynchronize(s), "synchronise");
+        for (int64_t i = 0; i < nb; ++i) total += part[i];
+    }
+    *count = total;
     return FK_OK;
 }
 

@@ -19,18 +19,34 @@ constexpr int kWave = 64;
 // Element size in bytes of a problem dtype.
 inline int dtype_size(int dtype) { return dtype == FK_F32 ? 4 : 2; }
 
+// Most sorted positions one wave reduces in the segment-sum kernel (a piece:
+// part of a single segment).
+constexpr int kSegRun = 256;
+// Pieces a problem can have: sum over segments of ceil(count / kSegRun).
+inline int64_t piece_capacity(int64_t N, int64_t K) { return (N + kSegRun - 1) / kSegRun + K; }
+
+// Counting sort plan: the tiled form (per-tile count table, no global
+// atomics) when K is small enough for LDS bins and the table stays modest.
+bool sort_tiled(int64_t N, int64_t K);
+// int32 entries per problem of the sort table (tile table or cursors), an
+// upper bound for every N' <= N
+int64_t sort_table_bound(int64_t N, int64_t K);
+
 // Workspace layout.  Every region starts on a 256-byte boundary.  Sizes grow
 // with B*K*d, B*N and B*K only: the N x K distance matrix has no place here.
 struct Workspace {
     float* bias;         // [B][K]   -0.5 |c|^2 of the centroids an assign reads
     int32_t* offsets;    // [B][K+1] segment starts of the sorted labels
-    int32_t* cursor;     // [B][K]   scatter cursors
+    int32_t* table;      // [B][sort_table_bound] per-tile counts or cursors
     int32_t* sorted_idx; // [B][N]   argsort of the labels
-    int32_t* sorted_lab; // [B][N]   label at each sorted position
+    int32_t* poff;       // [B][K+1] first piece of each segment
+    int32_t* pieces;     // [B][1 + 2 * piece_capacity] piece count, segments, starts
     float* sums;         // [B][K][d] fp32 segment sums
+    int32_t* arrive;     // [B][K]   pieces of each segment added so far
     int32_t* counts;     // [B][K]   counts when the caller passes none
     void* lowp;          // [B][K][d] centroids in the problem dtype (16-bit dtypes)
-    uint32_t* flags;     // [0] out-of-range labels, [1] max squared move (fp32 bits)
+    int32_t* bad;        // [B]      labels outside [0, K) per problem
+    uint32_t* flags;     // [1] max squared move (fp32 bits)
     size_t total;
 };
 
@@ -45,14 +61,43 @@ struct StreamWorkspace {
     float* sums;         // [B][K][d]
     int32_t* ccounts;    // [K]   counts of one chunk
     int32_t* offsets;    // [K+1] segment starts of one chunk
-    int32_t* cursor;     // [K]
+    int32_t* table;      // [sort_table_bound(chunk)]
     int32_t* sorted_idx; // [chunk]
-    int32_t* sorted_lab; // [chunk]
-    uint32_t* flags;     // [0] out-of-range labels
+    int32_t* poff;       // [K+1]
+    int32_t* pieces;     // [1 + 2 * piece_capacity(chunk)]
+    int32_t* bad;        // [1]
     size_t total;
 };
 
 StreamWorkspace stream_workspace_layout(const fk_problem& p, int64_t chunk, char* base);
+
+// Argument block of the counting sort.
+struct SortParams {
+    const int32_t* labels;  // [B][N]
+    int32_t* counts;        // [B][K]
+    int32_t* offsets;       // [B][K+1]
+    int32_t* sorted_idx;    // [B][N]
+    int32_t* poff;          // [B][K+1]
+    int32_t* pieces;        // [B][1 + 2 * piece_capacity]
+    int32_t* table;         // [B][sort_table_bound]
+    int32_t* bad;           // [B]
+    uint32_t* move;         // cleared when not null
+    uint32_t* zero[2];      // ranges cleared on the way (null = none)
+    int64_t zero_n[2];      // their lengths in 32-bit words
+};
+
+// Argument block of the segment sums.  final: fused finalize into C_next
+// (sums and arrive must be zero); otherwise partial sums are added to sums.
+struct SegParams {
+    bool final;
+    float* sums;
+    int32_t* arrive;
+    const float* C_prev;
+    float* C_next;
+    void* lowp;       // problem dtype, or null
+    float* bias;      // or null
+    uint32_t* move;   // or null
+};
 
 // ---- launchers (return hipSuccess or the launch error) ----------------------
 hipError_t launch_fill_u32(uint32_t* ptr, int64_t n, uint32_t value, hipStream_t s);
@@ -72,19 +117,12 @@ hipError_t launch_assign(int dtype, const void* X, const void* C, const float* b
                          int32_t* labels, float* min_dist, int64_t B, int64_t N, int64_t K, int d,
                          hipStream_t s);
 
-hipError_t launch_histogram(const int32_t* labels, int32_t* counts, uint32_t* flags, int64_t B,
-                            int64_t N, int64_t K, hipStream_t s);
-
-hipError_t launch_scan(const int32_t* counts, int32_t* offsets, int32_t* cursor, int64_t B,
-                       int64_t K, hipStream_t s);
-
-// sorted_lab may be NULL
-hipError_t launch_scatter(const int32_t* labels, int32_t* cursor, int32_t* sorted_idx,
-                          int32_t* sorted_lab, int64_t B, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_sort(const SortParams& sp, int64_t B, int64_t N, int64_t K, hipStream_t s);
 
 hipError_t launch_segment_sums(int dtype, const void* X, const int32_t* sorted_idx,
-                               const int32_t* sorted_lab, const int32_t* offsets, float* sums,
-                               int64_t B, int64_t N, int64_t K, int d, hipStream_t s);
+                               const int32_t* offsets, const int32_t* pieces,
+                               const SegParams& sp, int64_t B, int64_t N, int64_t K, int d,
+                               hipStream_t s);
 
 // C_next = sums / counts (or C_prev when empty); optional low-precision copy,
 // bias of the copy, squared-move maximum; clears the sums.

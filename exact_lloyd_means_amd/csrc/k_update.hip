@@ -8,20 +8,30 @@
 // one atomic add per piece: O((K + N/B_N) d) atomics instead of O(N d).
 //
 // MI355X design:
-//  * The argsort is a counting sort, since keys are small integers in [0, K):
-//    histogram (LDS-privatised) -> exclusive scan -> scatter, where each
-//    workgroup reserves one range per label with a single global atomic and
-//    ranks its elements inside that range with LDS atomics.  Order inside a
-//    segment is unspecified; the grouping is exact.
-//  * The gather-reduce gives every wave a fixed run of sorted positions.  The
-//    segment walk is wave-uniform (indices and offsets come through the
-//    scalar unit), lanes split the d dimensions of each row, rows are loaded
-//    several at a time for memory-level parallelism, and a piece ends with
-//    one row of fp32 atomic adds.
-//  * Finalize divides by the exact integer count (IEEE fp32 division), keeps
-//    empty centroids bit for bit, writes the round-to-nearest-even copy in
-//    the input dtype with its |c|^2 bias for the next assignment, tracks the
-//    largest squared centroid move and clears the sums for the next call.
+//  * The argsort is a counting sort, since keys are small integers in [0, K).
+//    Tiled form (K <= 16384 and a per-tile table of modest size): each
+//    workgroup histograms a tile of 4096 labels in LDS and writes the tile's
+//    counts; a column pass turns them into per-tile prefix counts; the
+//    scatter workgroup rescans the counts in LDS, so every label of its tile
+//    has a base position, and ranks its elements with LDS atomics.  No
+//    global atomics.  Otherwise (large K) the histogram uses global atomics
+//    and each scatter workgroup reserves one range per label with a single
+//    global atomic.  Order inside a segment is unspecified in both forms; the
+//    grouping is exact.
+//  * The gather-reduce gives every wave a fixed run of 256 sorted positions,
+//    so hot clusters spread over many waves.  The segment walk is
+//    wave-uniform (row indices come through readlane, segment boundaries
+//    from a window of offsets held in one VGPR), lanes split the d
+//    dimensions of each row, and rows are loaded a batch at a time for
+//    memory-level parallelism.
+//  * Fused finalize: a segment that lies inside one wave's run is finalized
+//    from registers; otherwise each piece adds its partial sum with one row
+//    of fp32 atomics and bumps the segment's arrival counter, and the last
+//    piece to arrive reads the total back and finalizes it.  Finalize divides
+//    by the exact integer count (IEEE fp32 division), writes the
+//    round-to-nearest-even copy in the input dtype with its |c|^2 bias for
+//    the next assignment, and tracks the largest squared centroid move;
+//    empty segments keep the previous centroid bit for bit.
 #include <math.h>
 
 #include "fk_internal.h"
@@ -32,8 +42,7 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kSortTile = 4096;          // labels per histogram / scatter workgroup
 constexpr int64_t kLdsBinsMax = 16384;   // LDS-privatised bins (64 KiB)
-constexpr int kSegChunk = 64;            // sorted positions per wave in the gather-reduce
-constexpr int kSegUnroll = 8;            // rows in flight per wave
+constexpr int64_t kTiledBinsMax = 16000; // tiled sort: bins + scan scratch stay under 64 KiB
 
 __device__ inline float wave_sum(float v) {
 #pragma unroll
@@ -57,6 +66,31 @@ __global__ void k_add_i32(int32_t* __restrict__ dst, const int32_t* __restrict__
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x)
         dst[i] += src[i];
+}
+
+// Zeroes up to four 32-bit ranges in one launch (the grid strides over each).
+struct ZeroRanges {
+    uint32_t* p[4];
+    int64_t n[4];
+};
+__global__ void k_zero(ZeroRanges z) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        for (int64_t i = i0; i < z.n[r]; i += stride) z.p[r][i] = 0u;
+}
+
+// Zeroes [lo, hi) of a 32-bit array, 16 bytes per store where aligned.
+__device__ inline void zero_slice(uint32_t* __restrict__ p, int64_t lo, int64_t hi) {
+    if (lo >= hi) return;
+    int64_t a = (lo + 3) & ~(int64_t)3;
+    if (a > hi) a = hi;
+    for (int64_t i = lo + threadIdx.x; i < a; i += blockDim.x) p[i] = 0u;
+    const int64_t b4 = a + ((hi - a) & ~(int64_t)3);
+    uint4* q = reinterpret_cast<uint4*>(p + a);
+    for (int64_t i = threadIdx.x; i < (b4 - a) / 4; i += blockDim.x) q[i] = make_uint4(0, 0, 0, 0);
+    for (int64_t i = b4 + threadIdx.x; i < hi; i += blockDim.x) p[i] = 0u;
 }
 
 // bias[row] = -0.5 * sum_j C[row][j]^2 in fp32 (one wave per centroid row)
@@ -96,11 +130,171 @@ __global__ __launch_bounds__(kBlock) void k_prepare(const float* __restrict__ C,
 }
 
 // ---------------------------------------------------------------------------
-// counts[b][k] += #{i in tile : labels[b][i] == k}; out-of-range labels are
-// counted in flags[0] and skipped.
+// Pieces of the segment sums: every nonempty segment [off[k], off[k+1]) is
+// cut into pieces of at most kSegRun sorted positions, one wave each.  The
+// piece block of a problem holds P[0] = number of pieces, P[1 + j] = the
+// segment of piece j and P[1 + M + j] = its first position (M = capacity);
+// poff[k] is the first piece of segment k.  Thread-strided over k; off may
+// live in LDS or global memory.
+__device__ inline void write_pieces(const int32_t* off, const int32_t* __restrict__ poff,
+                                    int64_t K, int32_t* __restrict__ P, int64_t M) {
+    for (int64_t k = threadIdx.x; k < K; k += blockDim.x) {
+        const int32_t s = off[k], e = off[k + 1];
+        int64_t j = poff[k];
+        for (int32_t p = s; p < e; p += kSegRun, ++j) {
+            P[1 + j] = (int32_t)k;
+            P[1 + M + j] = p;
+        }
+    }
+    if (threadIdx.x == 0) P[0] = poff[K];
+}
+
+// Block-wide exclusive scan of counts[0..K) into off[0..K] (LDS or global,
+// off[K] = total); with PIECES the scanned value of label k is its number
+// of pieces, ceil(counts[k] / kSegRun).  Each thread owns a contiguous range
+// of labels.
+template <bool PIECES>
+__device__ inline void block_offsets(const int32_t* __restrict__ counts, int64_t K,
+                                     int32_t* __restrict__ off, int32_t* __restrict__ s_part) {
+    auto val = [&](int64_t k) -> int32_t {
+        const int32_t c = counts[k];
+        return PIECES ? (c + kSegRun - 1) / kSegRun : c;
+    };
+    const int64_t per = (K + kBlock - 1) / kBlock;
+    const int64_t k0 = min((int64_t)threadIdx.x * per, K);
+    const int64_t k1 = min(k0 + per, K);
+    int32_t local = 0;
+    for (int64_t k = k0; k < k1; ++k) local += val(k);
+    s_part[threadIdx.x] = local;
+    __syncthreads();
+    for (int o = 1; o < kBlock; o <<= 1) {
+        const int32_t v = threadIdx.x >= o ? s_part[threadIdx.x - o] : 0;
+        __syncthreads();
+        s_part[threadIdx.x] += v;
+        __syncthreads();
+    }
+    int32_t run = s_part[threadIdx.x] - local;
+    for (int64_t k = k0; k < k1; ++k) {
+        off[k] = run;
+        run += val(k);
+    }
+    if (threadIdx.x == kBlock - 1) off[K] = s_part[kBlock - 1];
+    __syncthreads();
+}
+
+// ---- tiled counting sort ----------------------------------------------------
+// th[b][t][k] = #{i in tile t : labels[b][i] == k}, th[b][t][K] = labels out
+// of [0, K) in the tile.  The workgroups also zero the given 32-bit ranges
+// (the segment sums and arrival counters of the update that follows).
+__global__ __launch_bounds__(kBlock) void k_tile_hist(const int32_t* __restrict__ labels,
+                                                      int32_t* __restrict__ th, int64_t N,
+                                                      int64_t K, int64_t T, ZeroRanges z) {
+    extern __shared__ int32_t s_hist[];  // [K + 1]
+    const int64_t b = blockIdx.y;
+    const int64_t t = blockIdx.x;
+    for (int64_t k = threadIdx.x; k <= K; k += kBlock) s_hist[k] = 0;
+    __syncthreads();
+    const int64_t i0 = t * kSortTile;
+    const int64_t i1 = min(i0 + (int64_t)kSortTile, N);
+    const int32_t* lab = labels + b * N;
+    int32_t bad = 0;
+    for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
+        const int32_t a = lab[i];
+        if (a >= 0 && a < K)
+            atomicAdd(&s_hist[a], 1);
+        else
+            ++bad;
+    }
+    if (bad) atomicAdd(&s_hist[K], bad);
+    __syncthreads();
+    int32_t* out = th + (b * T + t) * (K + 1);
+    for (int64_t k = threadIdx.x; k <= K; k += kBlock) out[k] = s_hist[k];
+    // this workgroup's share of each range to clear
+    const int64_t wg = b * T + t, nwg = (int64_t)gridDim.y * T;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if (!z.n[r]) continue;
+        const int64_t per = ((z.n[r] + nwg - 1) / nwg + 3) & ~(int64_t)3;
+        zero_slice(z.p[r], min(wg * per, z.n[r]), min((wg + 1) * per, z.n[r]));
+    }
+}
+
+// Column pass: th[b][t][k] <- sum_{t' < t} th[b][t'][k]; counts[b][k] and
+// bad[b] (column K) receive the column totals.
+__global__ __launch_bounds__(kBlock) void k_tile_colscan(int32_t* __restrict__ th,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ bad, int64_t K,
+                                                         int64_t T) {
+    const int64_t b = blockIdx.y;
+    const int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (k > K) return;
+    int32_t* col = th + b * T * (K + 1) + k;
+    int32_t run = 0;
+    int64_t t = 0;
+    for (; t + 8 <= T; t += 8) {
+        int32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = col[(t + u) * (K + 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            col[(t + u) * (K + 1)] = run;
+            run += v[u];
+        }
+    }
+    for (; t < T; ++t) {
+        const int32_t v = col[t * (K + 1)];
+        col[t * (K + 1)] = run;
+        run += v;
+    }
+    if (k < K)
+        counts[b * K + k] = run;
+    else
+        bad[b] = run;
+}
+
+// Scatter of tile t: base of label k = offset[k] + th[b][t][k]; elements are
+// ranked with LDS atomics.  Tile 0 of every problem also publishes the
+// offsets and the pieces of the segment sums, and problem 0 clears the move
+// word.
+__global__ __launch_bounds__(kBlock) void k_tile_scatter(
+    const int32_t* __restrict__ labels, const int32_t* __restrict__ th,
+    const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_idx, int32_t* __restrict__ poff, int32_t* __restrict__ pieces,
+    uint32_t* __restrict__ move, int64_t N, int64_t K, int64_t T, int64_t M) {
+    extern __shared__ int32_t s_mem[];
+    int32_t* s_off = s_mem;              // [K + 1]
+    int32_t* s_part = s_mem + K + 1;     // [kBlock]
+    const int64_t b = blockIdx.y;
+    const int64_t t = blockIdx.x;
+    block_offsets<false>(counts + b * K, K, s_off, s_part);
+    if (t == 0) {
+        int32_t* off = offsets + b * (K + 1);
+        for (int64_t k = threadIdx.x; k <= K; k += kBlock) off[k] = s_off[k];
+        int32_t* po = poff + b * (K + 1);
+        block_offsets<true>(counts + b * K, K, po, s_part);
+        write_pieces(s_off, po, K, pieces + b * (2 * M + 1), M);
+        if (b == 0 && threadIdx.x == 0 && move) *move = 0u;
+    }
+    __syncthreads();
+    const int32_t* pre = th + (b * T + t) * (K + 1);
+    for (int64_t k = threadIdx.x; k < K; k += kBlock) s_off[k] += pre[k];
+    __syncthreads();
+    const int64_t i0 = t * kSortTile;
+    const int64_t i1 = min(i0 + (int64_t)kSortTile, N);
+    const int32_t* lab = labels + b * N;
+    int32_t* out = sorted_idx + b * N;
+    for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
+        const int32_t a = lab[i];
+        if (a >= 0 && a < K) out[atomicAdd(&s_off[a], 1)] = (int32_t)i;
+    }
+}
+
+// ---- counting sort with global atomics (large K) ----------------------------
+// counts[b][k] += #{i in tile : labels[b][i] == k}; labels out of [0, K) are
+// counted in bad[b] and skipped.
 __global__ __launch_bounds__(kBlock) void k_histogram(const int32_t* __restrict__ labels,
                                                       int32_t* __restrict__ counts,
-                                                      uint32_t* __restrict__ flags, int64_t N,
+                                                      int32_t* __restrict__ bad, int64_t N,
                                                       int64_t K, int use_lds) {
     extern __shared__ int32_t s_hist[];
     const int64_t b = blockIdx.y;
@@ -108,7 +302,7 @@ __global__ __launch_bounds__(kBlock) void k_histogram(const int32_t* __restrict_
     const int64_t i1 = min(i0 + (int64_t)kSortTile, N);
     const int32_t* lab = labels + b * N;
     int32_t* cnt = counts + b * K;
-    uint32_t bad = 0;
+    int32_t nbad = 0;
     if (use_lds) {
         for (int64_t k = threadIdx.x; k < K; k += kBlock) s_hist[k] = 0;
         __syncthreads();
@@ -117,7 +311,7 @@ __global__ __launch_bounds__(kBlock) void k_histogram(const int32_t* __restrict_
             if (a >= 0 && a < K)
                 atomicAdd(&s_hist[a], 1);
             else
-                ++bad;
+                ++nbad;
         }
         __syncthreads();
         for (int64_t k = threadIdx.x; k < K; k += kBlock) {
@@ -130,49 +324,36 @@ __global__ __launch_bounds__(kBlock) void k_histogram(const int32_t* __restrict_
             if (a >= 0 && a < K)
                 atomicAdd(&cnt[a], 1);
             else
-                ++bad;
+                ++nbad;
         }
     }
-    if (bad) atomicAdd(&flags[0], bad);
+    if (nbad) atomicAdd(&bad[b], nbad);
 }
 
-// offsets[b][k] = sum_{k' < k} counts[b][k'], offsets[b][K] = total; cursor = offsets
+// offsets[b] = exclusive scan of counts[b] (offsets[b][K] = total), cursor =
+// offsets, pieces of the segment sums; problem 0 clears the move word.
 __global__ __launch_bounds__(kBlock) void k_scan(const int32_t* __restrict__ counts,
                                                  int32_t* __restrict__ offsets,
-                                                 int32_t* __restrict__ cursor, int64_t K) {
-    __shared__ int32_t s[kBlock];
+                                                 int32_t* __restrict__ cursor,
+                                                 int32_t* __restrict__ poff,
+                                                 int32_t* __restrict__ pieces,
+                                                 uint32_t* __restrict__ move, int64_t K,
+                                                 int64_t M) {
+    __shared__ int32_t s_part[kBlock];
     const int64_t b = blockIdx.x;
-    const int32_t* c = counts + b * K;
     int32_t* off = offsets + b * (K + 1);
-    int32_t* cur = cursor + b * K;
-    const int64_t per = (K + kBlock - 1) / kBlock;
-    const int64_t k0 = min((int64_t)threadIdx.x * per, K);
-    const int64_t k1 = min(k0 + per, K);
-    int32_t local = 0;
-    for (int64_t k = k0; k < k1; ++k) local += c[k];
-    s[threadIdx.x] = local;
-    __syncthreads();
-    for (int o = 1; o < kBlock; o <<= 1) {
-        const int32_t v = threadIdx.x >= o ? s[threadIdx.x - o] : 0;
-        __syncthreads();
-        s[threadIdx.x] += v;
-        __syncthreads();
-    }
-    int32_t run = s[threadIdx.x] - local;
-    for (int64_t k = k0; k < k1; ++k) {
-        off[k] = run;
-        cur[k] = run;
-        run += c[k];
-    }
-    if (threadIdx.x == kBlock - 1) off[K] = s[kBlock - 1];
+    int32_t* po = poff + b * (K + 1);
+    block_offsets<false>(counts + b * K, K, off, s_part);
+    block_offsets<true>(counts + b * K, K, po, s_part);
+    for (int64_t k = threadIdx.x; k < K; k += kBlock) cursor[b * K + k] = off[k];
+    write_pieces(off, po, K, pieces + b * (2 * M + 1), M);
+    if (b == 0 && threadIdx.x == 0 && move) *move = 0u;
 }
 
-// sorted_idx[b][pos] = i with pos inside label a_i's segment; sorted_lab
-// (optional) receives the label at each sorted position
+// sorted_idx[b][pos] = i with pos inside label a_i's segment
 __global__ __launch_bounds__(kBlock) void k_scatter(const int32_t* __restrict__ labels,
                                                     int32_t* __restrict__ cursor,
-                                                    int32_t* __restrict__ sorted_idx,
-                                                    int32_t* __restrict__ sorted_lab, int64_t N,
+                                                    int32_t* __restrict__ sorted_idx, int64_t N,
                                                     int64_t K, int use_lds) {
     extern __shared__ int32_t s_base[];
     const int64_t b = blockIdx.y;
@@ -181,7 +362,6 @@ __global__ __launch_bounds__(kBlock) void k_scatter(const int32_t* __restrict__ 
     const int32_t* lab = labels + b * N;
     int32_t* cur = cursor + b * K;
     int32_t* out = sorted_idx + b * N;
-    int32_t* olab = sorted_lab ? sorted_lab + b * N : nullptr;
     if (use_lds) {
         for (int64_t k = threadIdx.x; k < K; k += kBlock) s_base[k] = 0;
         __syncthreads();
@@ -198,20 +378,12 @@ __global__ __launch_bounds__(kBlock) void k_scatter(const int32_t* __restrict__ 
         __syncthreads();
         for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
             const int32_t a = lab[i];
-            if (a >= 0 && a < K) {
-                const int32_t pos = atomicAdd(&s_base[a], 1);
-                out[pos] = (int32_t)i;
-                if (olab) olab[pos] = a;
-            }
+            if (a >= 0 && a < K) out[atomicAdd(&s_base[a], 1)] = (int32_t)i;
         }
     } else {
         for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
             const int32_t a = lab[i];
-            if (a >= 0 && a < K) {
-                const int32_t pos = atomicAdd(&cur[a], 1);
-                out[pos] = (int32_t)i;
-                if (olab) olab[pos] = a;
-            }
+            if (a >= 0 && a < K) out[atomicAdd(&cur[a], 1)] = (int32_t)i;
         }
     }
 }
@@ -245,85 +417,193 @@ constexpr int seg_batch() {
     return regs >= 64 ? 1 : 64 / regs;
 }
 
-// Each wave reduces kSegChunk = 64 consecutive sorted positions.  Its 64
-// point indices and labels arrive with one coalesced load (one per lane);
-// row addresses are then read lane by lane (readlane, no memory latency),
-// a batch of rows is loaded back to back, and the rows are added in order,
-// closing a piece with one row of atomic adds whenever the label changes.
-// sums must be zero on entry (or hold earlier partial sums to add to).
+// Where the segment sums go.  FINAL: the fused finalize writes the new
+// centroids (sums and arrive must be zero on entry).  Otherwise partial sums
+// are only added into sums (chunks of a streamed pass).
+template <typename T>
+struct SegOut {
+    float* sums;           // [B][K][d]
+    int32_t* arrive;       // [B][K]   FINAL
+    const float* C_prev;   // [B][K][d] FINAL
+    float* C_next;         // [B][K][d] FINAL
+    T* lowp;               // [B][K][d] or null
+    float* bias;           // [B][K] or null
+    uint32_t* move;        // max squared move (fp32 bits) or null
+};
+
+// Finalizes centroid row k of problem b from the lane's EPL sums.
 template <typename T, int EPL, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_segment_sums(const T* __restrict__ X,
-                                                         const int32_t* __restrict__ sorted_idx,
-                                                         const int32_t* __restrict__ sorted_lab,
-                                                         const int32_t* __restrict__ offsets,
-                                                         float* __restrict__ sums, int64_t N,
-                                                         int64_t K, int d) {
-    static_assert(kSegChunk == kWave, "one sorted position per lane");
+__device__ inline void finalize_row(const SegOut<T>& o, int64_t b, int64_t K, int d, int64_t k,
+                                    int32_t count, const float (&s)[EPL], int e0) {
+    const int64_t base = (b * K + k) * d;
+    const float fn = (float)count;
+    float cn = 0.f, mv = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        const int j = e0 + e;
+        if (j < d) {
+            const float c = s[e] / fn;
+            const float prev = o.C_prev[base + j];
+            o.C_next[base + j] = c;
+            float cq = c;
+            if (o.lowp) {
+                const T q = (T)c;
+                o.lowp[base + j] = q;
+                cq = to_f32(q);
+            }
+            cn = fmaf(cq, cq, cn);
+            const float m = c - prev;
+            mv = fmaf(m, m, mv);
+        }
+    }
+    if (o.bias) {
+        cn = wave_sum(cn);
+        if ((threadIdx.x & 63) == 0) o.bias[b * K + k] = -0.5f * cn;
+    }
+    if (o.move) {
+        mv = wave_sum(mv);
+        if ((threadIdx.x & 63) == 0) atomicMax(o.move, __float_as_uint(mv));
+    }
+}
+
+// One wave reduces one piece: at most kSegRun consecutive sorted positions
+// of a single segment, so the row loop has no boundary to test.  Row indices
+// arrive with coalesced loads (one per lane) and are read lane by lane
+// (readlane); a batch of RB rows is loaded back to back, then added in
+// order.  A segment of one piece is finalized from registers; otherwise the
+// piece adds its sums with one row of fp32 atomics, and with FINAL the last
+// piece to arrive finalizes the segment.  Extra workgroups past the pieces
+// (FINAL only) give empty segments their previous centroid.
+template <typename T, int EPL, bool VEC, bool FINAL>
+__global__ __launch_bounds__(kBlock) void k_segment_sums(
+    const T* __restrict__ X, const int32_t* __restrict__ sorted_idx,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ pieces, SegOut<T> o,
+    int64_t N, int64_t K, int d, int64_t M, int64_t piece_wgs) {
     constexpr int RB = seg_batch<T, EPL>();
+    constexpr int NV = kSegRun / kWave;  // index registers per lane
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t b = blockIdx.y;
-    // positions past offsets[K] exist only when out-of-range labels were skipped
-    const int64_t total = offsets[b * (K + 1) + K];
-    const int64_t p0 = ((int64_t)blockIdx.x * (kBlock / kWave) + wave) * kSegChunk;
-    if (p0 >= total) return;
-    const int n = (int)min((int64_t)kSegChunk, total - p0);  // positions of this wave
-    const T* __restrict__ Xb = X + b * N * d;
-    float* __restrict__ Sb = sums + b * K * d;
-    const int64_t q = p0 + min(lane, n - 1);
-    const int32_t vidx = sorted_idx[b * N + q];
-    const int32_t vlab = sorted_lab[b * N + q];
-
+    const int32_t* __restrict__ off = offsets + b * (K + 1);
     const int e0 = lane * EPL;
     const bool active = e0 < d;
+
+    if ((int64_t)blockIdx.x >= piece_wgs) {
+        // empty segments: keep the previous centroid (FINAL only)
+        if constexpr (FINAL) {
+            const int64_t k = ((int64_t)blockIdx.x - piece_wgs) * (kBlock / kWave) + wave;
+            if (k >= K || off[k + 1] != off[k]) return;
+            const int64_t base = (b * K + k) * d;
+            float cn = 0.f;
+            for (int j = lane; j < d; j += kWave) {
+                const float c = o.C_prev[base + j];
+                o.C_next[base + j] = c;
+                float cq = c;
+                if (o.lowp) {
+                    const T q = (T)c;
+                    o.lowp[base + j] = q;
+                    cq = to_f32(q);
+                }
+                cn = fmaf(cq, cq, cn);
+            }
+            if (o.bias) {
+                cn = wave_sum(cn);
+                if (lane == 0) o.bias[b * K + k] = -0.5f * cn;
+            }
+        }
+        return;
+    }
+
+    const int32_t* __restrict__ P = pieces + b * (2 * M + 1);
+    const int64_t j = (int64_t)blockIdx.x * (kBlock / kWave) + wave;
+    if (j >= P[0]) return;
+    const int32_t k = __builtin_amdgcn_readfirstlane(P[1 + j]);
+    const int32_t p0 = __builtin_amdgcn_readfirstlane(P[1 + M + j]);
+    const int32_t s0 = __builtin_amdgcn_readfirstlane(off[k]);
+    const int32_t s1 = __builtin_amdgcn_readfirstlane(off[k + 1]);
+    const int n = min(kSegRun, s1 - p0);  // rows of this piece
+    const T* __restrict__ Xb = X + b * N * d;
+    int32_t vidx[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+        vidx[v] = sorted_idx[b * N + p0 + min(v * kWave + lane, n - 1)];
+
     float acc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-    int32_t cur = __builtin_amdgcn_readfirstlane(vlab);
-
-    auto flush = [&](int32_t kk) {
-        if (active) {
-            float* dst = Sb + (int64_t)kk * d + e0;
+    // batches of RB rows: all loads first, unconditionally, so they are in
+    // flight together (positions past n re-read the last row, lanes past d
+    // read the row start; neither is ever added)
 #pragma unroll
-            for (int e = 0; e < EPL; ++e)
-                if (VEC || e0 + e < d) atomicAdd(dst + e, acc[e]);
-        }
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-    };
-
-#pragma unroll
-    for (int base = 0; base < kSegChunk; base += RB) {
+    for (int base = 0; base < kSegRun; base += RB) {
         if (base < n) {
-            // all loads of the batch first, unconditionally, so they are in
-            // flight together: positions past n re-read the last row and
-            // lanes past d read the row start; neither is ever added
             RowPart<T, EPL> v[RB];
 #pragma unroll
             for (int u = 0; u < RB; ++u) {
-                const int32_t row = __builtin_amdgcn_readlane(vidx, base + u);
+                const int pos = base + u;
+                const int32_t row = __builtin_amdgcn_readlane(vidx[pos / kWave], pos % kWave);
                 v[u] = load_row_part<T, EPL, VEC>(Xb, row, d, active ? e0 : 0);
             }
+            if (active) {
+                if (base + RB <= n) {
 #pragma unroll
-            for (int u = 0; u < RB; ++u) {
-                if (base + u < n) {
-                    const int32_t a = __builtin_amdgcn_readlane(vlab, base + u);
-                    if (a != cur) {
-                        flush(cur);
-                        cur = a;
-                    }
-                    if (active) {
+                    for (int u = 0; u < RB; ++u)
 #pragma unroll
                         for (int e = 0; e < EPL; ++e) acc[e] += to_f32(v[u].v[e]);
-                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < RB; ++u)
+                        if (base + u < n) {
+#pragma unroll
+                            for (int e = 0; e < EPL; ++e) acc[e] += to_f32(v[u].v[e]);
+                        }
                 }
             }
         }
     }
-    flush(cur);
+
+    const int32_t count = s1 - s0;
+    if (FINAL && count <= kSegRun) {
+        finalize_row<T, EPL, VEC>(o, b, K, d, k, count, acc, e0);
+        return;
+    }
+    float* dst = o.sums + (b * K + k) * d + e0;
+    if constexpr (FINAL) {
+        // Returning atomics: once their results are in, the adds are
+        // performed at the device coherence point, so the arrival increment
+        // below is ordered after them without a cache write-back fence.
+        float done = 0.f;
+        if (active) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+                if (VEC || e0 + e < d) done += atomicAdd(dst + e, acc[e]);
+        }
+        asm volatile("" ::"v"(done) : "memory");
+        const int32_t npieces = (count + kSegRun - 1) / kSegRun;
+        int32_t prior = 0;
+        if (lane == 0) prior = atomicAdd(o.arrive + b * K + k, 1);
+        prior = __builtin_amdgcn_readfirstlane(prior);
+        if (prior == npieces - 1) {
+            // every other piece added its sums before arriving
+            float t[EPL];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+                t[e] = active && (VEC || e0 + e < d)
+                           ? __hip_atomic_load(dst + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : 0.f;
+            finalize_row<T, EPL, VEC>(o, b, K, d, k, count, t, e0);
+        }
+    } else if (active) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            if (VEC || e0 + e < d) atomicAdd(dst + e, acc[e]);
+    }
 }
 
 // ---------------------------------------------------------------------------
+// Finalize of accumulated sums (streamed path): C_next = sums / counts (or
+// C_prev when empty), optional low-precision copy and its bias, squared move
+// maximum; clears the sums.
 template <typename T, bool LOWP>
 __global__ __launch_bounds__(kBlock) void k_finalize(float* __restrict__ sums,
                                                      const int32_t* __restrict__ counts,
@@ -369,23 +649,31 @@ inline unsigned grid_rows(int64_t rows) {
 }
 
 template <typename T>
-hipError_t segment_sums_t(const void* X, const int32_t* sorted_idx, const int32_t* sorted_lab,
-                          const int32_t* offsets, float* sums, int64_t B, int64_t N, int64_t K,
-                          int d, hipStream_t s) {
+hipError_t segment_sums_t(const void* X, const int32_t* sorted_idx, const int32_t* offsets,
+                          const int32_t* pieces, const SegParams& sp, int64_t B, int64_t N,
+                          int64_t K, int d, hipStream_t s) {
     const int epl = (d + kWave - 1) / kWave;
-    const dim3 grid((unsigned)((N + (int64_t)kSegChunk * (kBlock / kWave) - 1) /
-                               ((int64_t)kSegChunk * (kBlock / kWave))),
-                    (unsigned)B);
+    const int64_t M = piece_capacity(N, K);
+    const int64_t piece_wgs = (M + (kBlock / kWave) - 1) / (kBlock / kWave);
+    const int64_t row_wgs = sp.final ? (K + (kBlock / kWave) - 1) / (kBlock / kWave) : 0;
+    const dim3 grid((unsigned)(piece_wgs + row_wgs), (unsigned)B);
+    SegOut<T> o{sp.sums, sp.arrive, sp.C_prev, sp.C_next, static_cast<T*>(sp.lowp), sp.bias,
+                sp.move};
     const T* x = static_cast<const T*>(X);
-#define FK_SEG_CASE(E)                                                                        \
-    if (epl <= E) {                                                                           \
-        if (d % E == 0)                                                                       \
-            hipLaunchKernelGGL((k_segment_sums<T, E, true>), grid, dim3(kBlock), 0, s, x,     \
-                               sorted_idx, sorted_lab, offsets, sums, N, K, d);               \
-        else                                                                                  \
-            hipLaunchKernelGGL((k_segment_sums<T, E, false>), grid, dim3(kBlock), 0, s, x,    \
-                               sorted_idx, sorted_lab, offsets, sums, N, K, d);               \
-        return hipGetLastError();                                                             \
+#define FK_SEG_LAUNCH(E, V, F)                                                                 \
+    hipLaunchKernelGGL((k_segment_sums<T, E, V, F>), grid, dim3(kBlock), 0, s, x, sorted_idx,  \
+                       offsets, pieces, o, N, K, d, M, piece_wgs)
+#define FK_SEG_CASE(E)                                                                         \
+    if (epl <= E) {                                                                            \
+        const bool vec = d % E == 0;                                                           \
+        if (sp.final) {                                                                        \
+            if (vec) FK_SEG_LAUNCH(E, true, true);                                             \
+            else FK_SEG_LAUNCH(E, false, true);                                                \
+        } else {                                                                               \
+            if (vec) FK_SEG_LAUNCH(E, true, false);                                            \
+            else FK_SEG_LAUNCH(E, false, false);                                               \
+        }                                                                                      \
+        return hipGetLastError();                                                              \
     }
     FK_SEG_CASE(1)
     FK_SEG_CASE(2)
@@ -393,12 +681,24 @@ hipError_t segment_sums_t(const void* X, const int32_t* sorted_idx, const int32_
     FK_SEG_CASE(8)
     FK_SEG_CASE(16)
 #undef FK_SEG_CASE
+#undef FK_SEG_LAUNCH
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 // ---------------------------------------------------------------------------
+bool sort_tiled(int64_t N, int64_t K) {
+    const int64_t T = (N + kSortTile - 1) / kSortTile;
+    return K <= kTiledBinsMax && T * (K + 1) <= 4 * N + 65536;
+}
+
+int64_t sort_table_bound(int64_t N, int64_t K) {
+    const int64_t T = (N + kSortTile - 1) / kSortTile;
+    const int64_t tiled = min(T * (K + 1), 4 * N + 65536);
+    return tiled > K ? tiled : K;
+}
+
 hipError_t launch_fill_u32(uint32_t* ptr, int64_t n, uint32_t value, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     const int64_t blocks = min((n + kBlock - 1) / kBlock, (int64_t)4096);
@@ -447,42 +747,57 @@ hipError_t launch_prepare(int dtype, const float* C, void* lowp, float* bias, in
     return hipGetLastError();
 }
 
-hipError_t launch_histogram(const int32_t* labels, int32_t* counts, uint32_t* flags, int64_t B,
-                            int64_t N, int64_t K, hipStream_t s) {
+hipError_t launch_sort(const SortParams& sp, int64_t B, int64_t N, int64_t K, hipStream_t s) {
+    const int64_t T = (N + kSortTile - 1) / kSortTile;
+    const int64_t M = piece_capacity(N, K);
+    ZeroRanges z{};
+    for (int r = 0; r < 2; ++r) {
+        z.p[r] = sp.zero[r];
+        z.n[r] = sp.zero[r] ? sp.zero_n[r] : 0;
+    }
+    if (sort_tiled(N, K)) {
+        const dim3 tiles((unsigned)T, (unsigned)B);
+        hipLaunchKernelGGL(k_tile_hist, tiles, dim3(kBlock), (size_t)(K + 1) * sizeof(int32_t), s,
+                           sp.labels, sp.table, N, K, T, z);
+        hipLaunchKernelGGL(k_tile_colscan, dim3((unsigned)((K + kBlock) / kBlock), (unsigned)B),
+                           dim3(kBlock), 0, s, sp.table, sp.counts, sp.bad, K, T);
+        hipLaunchKernelGGL(k_tile_scatter, tiles, dim3(kBlock),
+                           (size_t)(K + 1 + kBlock) * sizeof(int32_t), s, sp.labels, sp.table,
+                           sp.counts, sp.offsets, sp.sorted_idx, sp.poff, sp.pieces, sp.move, N, K,
+                           T, M);
+        return hipGetLastError();
+    }
+    z.p[2] = reinterpret_cast<uint32_t*>(sp.counts);
+    z.n[2] = B * K;
+    z.p[3] = reinterpret_cast<uint32_t*>(sp.bad);
+    z.n[3] = B;
+    int64_t most = 0;
+    for (int r = 0; r < 4; ++r) most = z.n[r] > most ? z.n[r] : most;
+    const int64_t zb = min((most + kBlock - 1) / kBlock, (int64_t)4096);
+    hipLaunchKernelGGL(k_zero, dim3((unsigned)(zb > 0 ? zb : 1)), dim3(kBlock), 0, s, z);
     const int use_lds = K <= kLdsBinsMax;
     const size_t lds = use_lds ? (size_t)K * sizeof(int32_t) : 0;
-    const dim3 grid((unsigned)((N + kSortTile - 1) / kSortTile), (unsigned)B);
-    hipLaunchKernelGGL(k_histogram, grid, dim3(kBlock), lds, s, labels, counts, flags, N, K,
-                       use_lds);
-    return hipGetLastError();
-}
-
-hipError_t launch_scan(const int32_t* counts, int32_t* offsets, int32_t* cursor, int64_t B,
-                       int64_t K, hipStream_t s) {
-    hipLaunchKernelGGL(k_scan, dim3((unsigned)B), dim3(kBlock), 0, s, counts, offsets, cursor, K);
-    return hipGetLastError();
-}
-
-hipError_t launch_scatter(const int32_t* labels, int32_t* cursor, int32_t* sorted_idx,
-                          int32_t* sorted_lab, int64_t B, int64_t N, int64_t K, hipStream_t s) {
-    const int use_lds = K <= kLdsBinsMax;
-    const size_t lds = use_lds ? (size_t)K * sizeof(int32_t) : 0;
-    const dim3 grid((unsigned)((N + kSortTile - 1) / kSortTile), (unsigned)B);
-    hipLaunchKernelGGL(k_scatter, grid, dim3(kBlock), lds, s, labels, cursor, sorted_idx,
-                       sorted_lab, N, K, use_lds);
+    const dim3 tiles((unsigned)T, (unsigned)B);
+    hipLaunchKernelGGL(k_histogram, tiles, dim3(kBlock), lds, s, sp.labels, sp.counts, sp.bad, N,
+                       K, use_lds);
+    hipLaunchKernelGGL(k_scan, dim3((unsigned)B), dim3(kBlock), 0, s, sp.counts, sp.offsets,
+                       sp.table, sp.poff, sp.pieces, sp.move, K, M);
+    hipLaunchKernelGGL(k_scatter, tiles, dim3(kBlock), lds, s, sp.labels, sp.table, sp.sorted_idx,
+                       N, K, use_lds);
     return hipGetLastError();
 }
 
 hipError_t launch_segment_sums(int dtype, const void* X, const int32_t* sorted_idx,
-                               const int32_t* sorted_lab, const int32_t* offsets, float* sums,
-                               int64_t B, int64_t N, int64_t K, int d, hipStream_t s) {
+                               const int32_t* offsets, const int32_t* pieces,
+                               const SegParams& sp, int64_t B, int64_t N, int64_t K, int d,
+                               hipStream_t s) {
     switch (dtype) {
         case FK_F32:
-            return segment_sums_t<float>(X, sorted_idx, sorted_lab, offsets, sums, B, N, K, d, s);
+            return segment_sums_t<float>(X, sorted_idx, offsets, pieces, sp, B, N, K, d, s);
         case FK_F16:
-            return segment_sums_t<_Float16>(X, sorted_idx, sorted_lab, offsets, sums, B, N, K, d, s);
+            return segment_sums_t<_Float16>(X, sorted_idx, offsets, pieces, sp, B, N, K, d, s);
         default:
-            return segment_sums_t<__bf16>(X, sorted_idx, sorted_lab, offsets, sums, B, N, K, d, s);
+            return segment_sums_t<__bf16>(X, sorted_idx, offsets, pieces, sp, B, N, K, d, s);
     }
 }
 
