@@ -44,6 +44,8 @@ Workspace workspace_layout(const fk_problem& p, char* base) {
     w.poff = reinterpret_cast<int32_t*>(take(B * (K + 1) * sizeof(int32_t)));
     w.pieces = reinterpret_cast<int32_t*>(
         take(B * (1 + 2 * (size_t)piece_capacity(p.N, p.K)) * sizeof(int32_t)));
+    w.clear = reinterpret_cast<int32_t*>(
+        take(B * (1 + (size_t)piece_capacity(p.N, p.K)) * sizeof(int32_t)));
     w.sums = reinterpret_cast<float*>(take(B * K * d * sizeof(float)));
     w.arrive = reinterpret_cast<int32_t*>(take(B * K * sizeof(int32_t)));
     w.counts = reinterpret_cast<int32_t*>(take(B * K * sizeof(int32_t)));
@@ -153,8 +155,9 @@ fk_status check_assign_d(const fk_problem&) { return FK_OK; }
     } while (0)
 
 // Counting-sort argsort of the labels into counts, offsets, sorted_idx and
-// the run labels of the segment sums; optionally clears the sums and arrival
-// counters of a fused update and the move word on the way.
+// the pieces of the segment sums; with clear_update the sum rows and arrival
+// counters a fused update accumulates into are cleared on the way, and a
+// non-null move word is cleared.
 fk_status enqueue_sort(const fk_problem& p, const Workspace& w, const int32_t* labels,
                        int32_t* counts, int32_t* offsets, int32_t* sorted_idx, bool clear_update,
                        uint32_t* move, hipStream_t s) {
@@ -169,10 +172,10 @@ fk_status enqueue_sort(const fk_problem& p, const Workspace& w, const int32_t* l
     sp.bad = w.bad;
     sp.move = move;
     if (clear_update) {
-        sp.zero[0] = reinterpret_cast<uint32_t*>(w.sums);
-        sp.zero_n[0] = p.B * p.K * p.d;
-        sp.zero[1] = reinterpret_cast<uint32_t*>(w.arrive);
-        sp.zero_n[1] = p.B * p.K;
+        sp.sums = w.sums;
+        sp.arrive = w.arrive;
+        sp.clear = w.clear;
+        sp.d = p.d;
     }
     FK_TRY(launch_sort(sp, p.B, p.N, p.K, s), "sort labels");
     return FK_OK;

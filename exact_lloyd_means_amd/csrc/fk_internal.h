@@ -41,6 +41,7 @@ struct Workspace {
     int32_t* sorted_idx; // [B][N]   argsort of the labels
     int32_t* poff;       // [B][K+1] first piece of each segment
     int32_t* pieces;     // [B][1 + 2 * piece_capacity] piece count, segments, starts
+    int32_t* clear;      // [B][1 + piece_capacity] segments whose sum rows to clear
     float* sums;         // [B][K][d] fp32 segment sums
     int32_t* arrive;     // [B][K]   pieces of each segment added so far
     int32_t* counts;     // [B][K]   counts when the caller passes none
@@ -82,8 +83,10 @@ struct SortParams {
     int32_t* table;         // [B][sort_table_bound]
     int32_t* bad;           // [B]
     uint32_t* move;         // cleared when not null
-    uint32_t* zero[2];      // ranges cleared on the way (null = none)
-    int64_t zero_n[2];      // their lengths in 32-bit words
+    float* sums;            // [B][K][d] rows of multi-piece segments cleared (or null)
+    int32_t* arrive;        // [B][K]   their arrival counters cleared
+    int32_t* clear;         // [B][1 + piece_capacity] list of those segments
+    int64_t d;
 };
 
 // Argument block of the segment sums.  final: fused finalize into C_next

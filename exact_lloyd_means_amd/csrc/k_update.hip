@@ -41,6 +41,7 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kSortTile = 4096;          // labels per histogram / scatter workgroup
+constexpr int kSortPer = kSortTile / kBlock;  // labels per thread of a sort tile
 constexpr int64_t kLdsBinsMax = 16384;   // LDS-privatised bins (64 KiB)
 constexpr int64_t kTiledBinsMax = 16000; // tiled sort: bins + scan scratch stay under 64 KiB
 
@@ -79,18 +80,6 @@ __global__ void k_zero(ZeroRanges z) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
         for (int64_t i = i0; i < z.n[r]; i += stride) z.p[r][i] = 0u;
-}
-
-// Zeroes [lo, hi) of a 32-bit array, 16 bytes per store where aligned.
-__device__ inline void zero_slice(uint32_t* __restrict__ p, int64_t lo, int64_t hi) {
-    if (lo >= hi) return;
-    int64_t a = (lo + 3) & ~(int64_t)3;
-    if (a > hi) a = hi;
-    for (int64_t i = lo + threadIdx.x; i < a; i += blockDim.x) p[i] = 0u;
-    const int64_t b4 = a + ((hi - a) & ~(int64_t)3);
-    uint4* q = reinterpret_cast<uint4*>(p + a);
-    for (int64_t i = threadIdx.x; i < (b4 - a) / 4; i += blockDim.x) q[i] = make_uint4(0, 0, 0, 0);
-    for (int64_t i = b4 + threadIdx.x; i < hi; i += blockDim.x) p[i] = 0u;
 }
 
 // bias[row] = -0.5 * sum_j C[row][j]^2 in fp32 (one wave per centroid row)
@@ -134,10 +123,17 @@ __global__ __launch_bounds__(kBlock) void k_prepare(const float* __restrict__ C,
 // cut into pieces of at most kSegRun sorted positions, one wave each.  The
 // piece block of a problem holds P[0] = number of pieces, P[1 + j] = the
 // segment of piece j and P[1 + M + j] = its first position (M = capacity);
-// poff[k] is the first piece of segment k.  Thread-strided over k; off may
-// live in LDS or global memory.
+// poff[k] is the first piece of segment k.  Segments of several pieces are
+// the only ones the segment sums accumulate into; when clear is not null
+// they are listed there (clear[0] = n, clear[1..n] = segments) so the next
+// kernel can clear their sum rows and arrival counters.  Thread-strided over
+// k; off may live in LDS or global memory.
 __device__ inline void write_pieces(const int32_t* off, const int32_t* __restrict__ poff,
-                                    int64_t K, int32_t* __restrict__ P, int64_t M) {
+                                    int64_t K, int32_t* __restrict__ P, int64_t M,
+                                    int32_t* __restrict__ clear) {
+    __shared__ int32_t s_n;
+    if (threadIdx.x == 0) s_n = 0;
+    __syncthreads();
     for (int64_t k = threadIdx.x; k < K; k += blockDim.x) {
         const int32_t s = off[k], e = off[k + 1];
         int64_t j = poff[k];
@@ -145,8 +141,27 @@ __device__ inline void write_pieces(const int32_t* off, const int32_t* __restric
             P[1 + j] = (int32_t)k;
             P[1 + M + j] = p;
         }
+        if (clear && e - s > kSegRun) clear[1 + atomicAdd(&s_n, 1)] = (int32_t)k;
     }
     if (threadIdx.x == 0) P[0] = poff[K];
+    __syncthreads();
+    if (clear && threadIdx.x == 0) clear[0] = s_n;
+}
+
+// Clears the sum rows and arrival counters listed by write_pieces: this
+// workgroup's share, one wave per row.
+__device__ inline void clear_listed(const int32_t* __restrict__ clear, float* __restrict__ sums,
+                                    int32_t* __restrict__ arrive, int64_t d, int64_t wg,
+                                    int64_t nwg) {
+    const int n = clear[0];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int nw = blockDim.x / kWave;
+    for (int64_t r = wg * nw + threadIdx.x / kWave; r < n; r += nwg * nw) {
+        const int32_t k = clear[1 + r];
+        float* row = sums + (int64_t)k * d;
+        for (int64_t c = lane; c < d; c += kWave) row[c] = 0.f;
+        if (lane == 0) arrive[k] = 0;
+    }
 }
 
 // Block-wide exclusive scan of counts[0..K) into off[0..K] (LDS or global,
@@ -184,11 +199,10 @@ __device__ inline void block_offsets(const int32_t* __restrict__ counts, int64_t
 
 // ---- tiled counting sort ----------------------------------------------------
 // th[b][t][k] = #{i in tile t : labels[b][i] == k}, th[b][t][K] = labels out
-// of [0, K) in the tile.  The workgroups also zero the given 32-bit ranges
-// (the segment sums and arrival counters of the update that follows).
+// of [0, K) in the tile.
 __global__ __launch_bounds__(kBlock) void k_tile_hist(const int32_t* __restrict__ labels,
                                                       int32_t* __restrict__ th, int64_t N,
-                                                      int64_t K, int64_t T, ZeroRanges z) {
+                                                      int64_t K, int64_t T) {
     extern __shared__ int32_t s_hist[];  // [K + 1]
     const int64_t b = blockIdx.y;
     const int64_t t = blockIdx.x;
@@ -197,26 +211,27 @@ __global__ __launch_bounds__(kBlock) void k_tile_hist(const int32_t* __restrict_
     const int64_t i0 = t * kSortTile;
     const int64_t i1 = min(i0 + (int64_t)kSortTile, N);
     const int32_t* lab = labels + b * N;
+    // all label loads first, so they are in flight together
+    int32_t a[kSortPer];
+#pragma unroll
+    for (int j = 0; j < kSortPer; ++j) {
+        const int64_t i = i0 + threadIdx.x + j * kBlock;
+        a[j] = i < i1 ? lab[i] : 0;
+    }
     int32_t bad = 0;
-    for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
-        const int32_t a = lab[i];
-        if (a >= 0 && a < K)
-            atomicAdd(&s_hist[a], 1);
-        else
-            ++bad;
+#pragma unroll
+    for (int j = 0; j < kSortPer; ++j) {
+        if (i0 + threadIdx.x + j * kBlock < i1) {
+            if (a[j] >= 0 && a[j] < K)
+                atomicAdd(&s_hist[a[j]], 1);
+            else
+                ++bad;
+        }
     }
     if (bad) atomicAdd(&s_hist[K], bad);
     __syncthreads();
     int32_t* out = th + (b * T + t) * (K + 1);
     for (int64_t k = threadIdx.x; k <= K; k += kBlock) out[k] = s_hist[k];
-    // this workgroup's share of each range to clear
-    const int64_t wg = b * T + t, nwg = (int64_t)gridDim.y * T;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        if (!z.n[r]) continue;
-        const int64_t per = ((z.n[r] + nwg - 1) / nwg + 3) & ~(int64_t)3;
-        zero_slice(z.p[r], min(wg * per, z.n[r]), min((wg + 1) * per, z.n[r]));
-    }
 }
 
 // Column pass: th[b][t][k] <- sum_{t' < t} th[b][t'][k]; counts[b][k] and
@@ -252,40 +267,76 @@ __global__ __launch_bounds__(kBlock) void k_tile_colscan(int32_t* __restrict__ t
         bad[b] = run;
 }
 
-// Scatter of tile t: base of label k = offset[k] + th[b][t][k]; elements are
-// ranked with LDS atomics.  Tile 0 of every problem also publishes the
-// offsets and the pieces of the segment sums, and problem 0 clears the move
-// word.
+// Plan of one problem (one workgroup each): offsets = exclusive scan of the
+// counts, the pieces of the segment sums and the list of sum rows to clear;
+// problem 0 clears the move word.
+// With use_lds the counts and both scans live in LDS (3K + 2 words), so the
+// dependent steps wait on LDS rather than on global memory.
+__global__ __launch_bounds__(kBlock) void k_plan(const int32_t* __restrict__ counts,
+                                                 int32_t* __restrict__ offsets,
+                                                 int32_t* __restrict__ poff,
+                                                 int32_t* __restrict__ pieces,
+                                                 int32_t* __restrict__ clear,
+                                                 uint32_t* __restrict__ move, int64_t K,
+                                                 int64_t M, int use_lds) {
+    __shared__ int32_t s_part[kBlock];
+    extern __shared__ int32_t s_plan[];
+    const int64_t b = blockIdx.x;
+    int32_t* off = offsets + b * (K + 1);
+    int32_t* po = poff + b * (K + 1);
+    const int32_t* cnt = counts + b * K;
+    int32_t* l_off = off;
+    int32_t* l_po = po;
+    if (use_lds) {
+        int32_t* l_cnt = s_plan;
+        l_off = s_plan + K;
+        l_po = s_plan + 2 * K + 1;
+        for (int64_t k = threadIdx.x; k < K; k += kBlock) l_cnt[k] = cnt[k];
+        __syncthreads();
+        cnt = l_cnt;
+    }
+    block_offsets<false>(cnt, K, l_off, s_part);
+    block_offsets<true>(cnt, K, l_po, s_part);
+    write_pieces(l_off, l_po, K, pieces + b * (2 * M + 1), M, clear ? clear + b * (M + 1) : nullptr);
+    if (use_lds) {
+        for (int64_t k = threadIdx.x; k <= K; k += kBlock) {
+            off[k] = l_off[k];
+            po[k] = l_po[k];
+        }
+    }
+    if (b == 0 && threadIdx.x == 0 && move) *move = 0u;
+}
+
+// Scatter of tile t: base of label k = offsets[k] + th[b][t][k]; elements
+// are ranked with LDS atomics.  The workgroups also clear the listed sum
+// rows (clear may be null).
 __global__ __launch_bounds__(kBlock) void k_tile_scatter(
     const int32_t* __restrict__ labels, const int32_t* __restrict__ th,
-    const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_idx, int32_t* __restrict__ poff, int32_t* __restrict__ pieces,
-    uint32_t* __restrict__ move, int64_t N, int64_t K, int64_t T, int64_t M) {
-    extern __shared__ int32_t s_mem[];
-    int32_t* s_off = s_mem;              // [K + 1]
-    int32_t* s_part = s_mem + K + 1;     // [kBlock]
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_idx,
+    const int32_t* __restrict__ clear, float* __restrict__ sums, int32_t* __restrict__ arrive,
+    int64_t N, int64_t K, int64_t T, int64_t M, int64_t d) {
+    extern __shared__ int32_t s_base[];  // [K]
     const int64_t b = blockIdx.y;
     const int64_t t = blockIdx.x;
-    block_offsets<false>(counts + b * K, K, s_off, s_part);
-    if (t == 0) {
-        int32_t* off = offsets + b * (K + 1);
-        for (int64_t k = threadIdx.x; k <= K; k += kBlock) off[k] = s_off[k];
-        int32_t* po = poff + b * (K + 1);
-        block_offsets<true>(counts + b * K, K, po, s_part);
-        write_pieces(s_off, po, K, pieces + b * (2 * M + 1), M);
-        if (b == 0 && threadIdx.x == 0 && move) *move = 0u;
-    }
-    __syncthreads();
+    if (clear) clear_listed(clear + b * (M + 1), sums + b * K * d, arrive + b * K, d, t, T);
     const int32_t* pre = th + (b * T + t) * (K + 1);
-    for (int64_t k = threadIdx.x; k < K; k += kBlock) s_off[k] += pre[k];
+    const int32_t* off = offsets + b * (K + 1);
+    for (int64_t k = threadIdx.x; k < K; k += kBlock) s_base[k] = off[k] + pre[k];
     __syncthreads();
     const int64_t i0 = t * kSortTile;
     const int64_t i1 = min(i0 + (int64_t)kSortTile, N);
     const int32_t* lab = labels + b * N;
     int32_t* out = sorted_idx + b * N;
-    for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
-        const int32_t a = lab[i];
-        if (a >= 0 && a < K) out[atomicAdd(&s_off[a], 1)] = (int32_t)i;
+    int32_t a[kSortPer];
+#pragma unroll
+    for (int j = 0; j < kSortPer; ++j) {
+        const int64_t i = i0 + threadIdx.x + j * kBlock;
+        a[j] = i < i1 ? lab[i] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kSortPer; ++j) {
+        const int64_t i = i0 + threadIdx.x + j * kBlock;
+        if (a[j] >= 0 && a[j] < K) out[atomicAdd(&s_base[a[j]], 1)] = (int32_t)i;
     }
 }
 
@@ -330,33 +381,28 @@ __global__ __launch_bounds__(kBlock) void k_histogram(const int32_t* __restrict_
     if (nbad) atomicAdd(&bad[b], nbad);
 }
 
-// offsets[b] = exclusive scan of counts[b] (offsets[b][K] = total), cursor =
-// offsets, pieces of the segment sums; problem 0 clears the move word.
-__global__ __launch_bounds__(kBlock) void k_scan(const int32_t* __restrict__ counts,
-                                                 int32_t* __restrict__ offsets,
-                                                 int32_t* __restrict__ cursor,
-                                                 int32_t* __restrict__ poff,
-                                                 int32_t* __restrict__ pieces,
-                                                 uint32_t* __restrict__ move, int64_t K,
-                                                 int64_t M) {
-    __shared__ int32_t s_part[kBlock];
-    const int64_t b = blockIdx.x;
-    int32_t* off = offsets + b * (K + 1);
-    int32_t* po = poff + b * (K + 1);
-    block_offsets<false>(counts + b * K, K, off, s_part);
-    block_offsets<true>(counts + b * K, K, po, s_part);
-    for (int64_t k = threadIdx.x; k < K; k += kBlock) cursor[b * K + k] = off[k];
-    write_pieces(off, po, K, pieces + b * (2 * M + 1), M);
-    if (b == 0 && threadIdx.x == 0 && move) *move = 0u;
+// cursor = offsets (global-atomic scatter)
+__global__ void k_cursor(const int32_t* __restrict__ offsets, int32_t* __restrict__ cursor,
+                         int64_t K) {
+    const int64_t b = blockIdx.y;
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < K;
+         k += (int64_t)gridDim.x * blockDim.x)
+        cursor[b * K + k] = offsets[b * (K + 1) + k];
 }
 
 // sorted_idx[b][pos] = i with pos inside label a_i's segment
 __global__ __launch_bounds__(kBlock) void k_scatter(const int32_t* __restrict__ labels,
                                                     int32_t* __restrict__ cursor,
-                                                    int32_t* __restrict__ sorted_idx, int64_t N,
-                                                    int64_t K, int use_lds) {
+                                                    int32_t* __restrict__ sorted_idx,
+                                                    const int32_t* __restrict__ clear,
+                                                    float* __restrict__ sums,
+                                                    int32_t* __restrict__ arrive, int64_t N,
+                                                    int64_t K, int64_t M, int64_t d, int use_lds) {
     extern __shared__ int32_t s_base[];
     const int64_t b = blockIdx.y;
+    if (clear)
+        clear_listed(clear + b * (M + 1), sums + b * K * d, arrive + b * K, d, blockIdx.x,
+                     gridDim.x);
     const int64_t i0 = (int64_t)blockIdx.x * kSortTile;
     const int64_t i1 = min(i0 + (int64_t)kSortTile, N);
     const int32_t* lab = labels + b * N;
@@ -406,6 +452,37 @@ __device__ inline RowPart<T, EPL> load_row_part(const T* __restrict__ base, int6
     } else {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) r.v[e] = (e0 + e < d) ? p[e] : (T)0;
+    }
+    return r;
+}
+
+// The same through a buffer resource: the row's byte offset is wave-uniform
+// and goes in the scalar offset, the lane's part of the row in the vector
+// offset, so a row load costs no vector address arithmetic.  Needs the
+// problem's rows to span less than 2 GiB and whole EPL parts (d % EPL == 0).
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <typename T, int EPL>
+__device__ inline RowPart<T, EPL> load_row_part_buf(__amdgpu_buffer_rsrc_t rsrc, int32_t row_off,
+                                                    int32_t lane_off) {
+    constexpr int BYTES = EPL * (int)sizeof(T);
+    RowPart<T, EPL> r;
+    if constexpr (BYTES == 2) {
+        const uint16_t v = __builtin_amdgcn_raw_buffer_load_b16(rsrc, lane_off, row_off, 0);
+        __builtin_memcpy(r.v, &v, 2);
+    } else if constexpr (BYTES == 4) {
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(rsrc, lane_off, row_off, 0);
+        __builtin_memcpy(r.v, &v, 4);
+    } else if constexpr (BYTES == 8) {
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, lane_off, row_off, 0);
+        __builtin_memcpy(r.v, &v, 8);
+    } else {
+        static_assert(BYTES % 16 == 0, "row part of 16-byte chunks");
+        u32x4_t v[BYTES / 16];
+#pragma unroll
+        for (int c = 0; c < BYTES / 16; ++c)
+            v[c] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off + 16 * c, row_off, 0);
+        __builtin_memcpy(r.v, v, BYTES);
     }
     return r;
 }
@@ -474,6 +551,8 @@ __device__ inline void finalize_row(const SegOut<T>& o, int64_t b, int64_t K, in
 // piece adds its sums with one row of fp32 atomics, and with FINAL the last
 // piece to arrive finalizes the segment.  Extra workgroups past the pieces
 // (FINAL only) give empty segments their previous centroid.
+// VEC: rows load through a buffer resource (d % EPL == 0 and the problem's
+// rows span less than 2 GiB); otherwise element by element with bounds.
 template <typename T, int EPL, bool VEC, bool FINAL>
 __global__ __launch_bounds__(kBlock) void k_segment_sums(
     const T* __restrict__ X, const int32_t* __restrict__ sorted_idx,
@@ -523,6 +602,12 @@ __global__ __launch_bounds__(kBlock) void k_segment_sums(
     const int32_t s1 = __builtin_amdgcn_readfirstlane(off[k + 1]);
     const int n = min(kSegRun, s1 - p0);  // rows of this piece
     const T* __restrict__ Xb = X + b * N * d;
+    __amdgpu_buffer_rsrc_t rsrc;
+    if constexpr (VEC)
+        rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(Xb), 0,
+                                                 (int32_t)(N * d * (int64_t)sizeof(T)), 0x00020000);
+    const int32_t rowb = d * (int32_t)sizeof(T);
+    const int32_t lane_off = (active ? e0 : 0) * (int32_t)sizeof(T);
     int32_t vidx[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v)
@@ -542,7 +627,10 @@ __global__ __launch_bounds__(kBlock) void k_segment_sums(
             for (int u = 0; u < RB; ++u) {
                 const int pos = base + u;
                 const int32_t row = __builtin_amdgcn_readlane(vidx[pos / kWave], pos % kWave);
-                v[u] = load_row_part<T, EPL, VEC>(Xb, row, d, active ? e0 : 0);
+                if constexpr (VEC)
+                    v[u] = load_row_part_buf<T, EPL>(rsrc, row * rowb, lane_off);
+                else
+                    v[u] = load_row_part<T, EPL, false>(Xb, row, d, active ? e0 : 0);
             }
             if (active) {
                 if (base + RB <= n) {
@@ -663,9 +751,11 @@ hipError_t segment_sums_t(const void* X, const int32_t* sorted_idx, const int32_
 #define FK_SEG_LAUNCH(E, V, F)                                                                 \
     hipLaunchKernelGGL((k_segment_sums<T, E, V, F>), grid, dim3(kBlock), 0, s, x, sorted_idx,  \
                        offsets, pieces, o, N, K, d, M, piece_wgs)
+    // buffer loads need whole parts and rows spanning less than 2 GiB per problem
+    const bool buf_ok = N * (int64_t)d * (int64_t)sizeof(T) < ((int64_t)1 << 31);
 #define FK_SEG_CASE(E)                                                                         \
     if (epl <= E) {                                                                            \
-        const bool vec = d % E == 0;                                                           \
+        const bool vec = d % E == 0 && buf_ok;                                                 \
         if (sp.final) {                                                                        \
             if (vec) FK_SEG_LAUNCH(E, true, true);                                             \
             else FK_SEG_LAUNCH(E, false, true);                                                \
@@ -750,40 +840,43 @@ hipError_t launch_prepare(int dtype, const float* C, void* lowp, float* bias, in
 hipError_t launch_sort(const SortParams& sp, int64_t B, int64_t N, int64_t K, hipStream_t s) {
     const int64_t T = (N + kSortTile - 1) / kSortTile;
     const int64_t M = piece_capacity(N, K);
-    ZeroRanges z{};
-    for (int r = 0; r < 2; ++r) {
-        z.p[r] = sp.zero[r];
-        z.n[r] = sp.zero[r] ? sp.zero_n[r] : 0;
-    }
-    if (sort_tiled(N, K)) {
-        const dim3 tiles((unsigned)T, (unsigned)B);
-        hipLaunchKernelGGL(k_tile_hist, tiles, dim3(kBlock), (size_t)(K + 1) * sizeof(int32_t), s,
-                           sp.labels, sp.table, N, K, T, z);
-        hipLaunchKernelGGL(k_tile_colscan, dim3((unsigned)((K + kBlock) / kBlock), (unsigned)B),
-                           dim3(kBlock), 0, s, sp.table, sp.counts, sp.bad, K, T);
-        hipLaunchKernelGGL(k_tile_scatter, tiles, dim3(kBlock),
-                           (size_t)(K + 1 + kBlock) * sizeof(int32_t), s, sp.labels, sp.table,
-                           sp.counts, sp.offsets, sp.sorted_idx, sp.poff, sp.pieces, sp.move, N, K,
-                           T, M);
-        return hipGetLastError();
-    }
-    z.p[2] = reinterpret_cast<uint32_t*>(sp.counts);
-    z.n[2] = B * K;
-    z.p[3] = reinterpret_cast<uint32_t*>(sp.bad);
-    z.n[3] = B;
-    int64_t most = 0;
-    for (int r = 0; r < 4; ++r) most = z.n[r] > most ? z.n[r] : most;
-    const int64_t zb = min((most + kBlock - 1) / kBlock, (int64_t)4096);
-    hipLaunchKernelGGL(k_zero, dim3((unsigned)(zb > 0 ? zb : 1)), dim3(kBlock), 0, s, z);
+    const dim3 tiles((unsigned)T, (unsigned)B);
+    const bool tiled = sort_tiled(N, K);
     const int use_lds = K <= kLdsBinsMax;
     const size_t lds = use_lds ? (size_t)K * sizeof(int32_t) : 0;
-    const dim3 tiles((unsigned)T, (unsigned)B);
-    hipLaunchKernelGGL(k_histogram, tiles, dim3(kBlock), lds, s, sp.labels, sp.counts, sp.bad, N,
-                       K, use_lds);
-    hipLaunchKernelGGL(k_scan, dim3((unsigned)B), dim3(kBlock), 0, s, sp.counts, sp.offsets,
-                       sp.table, sp.poff, sp.pieces, sp.move, K, M);
-    hipLaunchKernelGGL(k_scatter, tiles, dim3(kBlock), lds, s, sp.labels, sp.table, sp.sorted_idx,
-                       N, K, use_lds);
+    if (tiled) {
+        hipLaunchKernelGGL(k_tile_hist, tiles, dim3(kBlock), (size_t)(K + 1) * sizeof(int32_t), s,
+                           sp.labels, sp.table, N, K, T);
+        hipLaunchKernelGGL(k_tile_colscan, dim3((unsigned)((K + kBlock) / kBlock), (unsigned)B),
+                           dim3(kBlock), 0, s, sp.table, sp.counts, sp.bad, K, T);
+    } else {
+        ZeroRanges z{};
+        z.p[0] = reinterpret_cast<uint32_t*>(sp.counts);
+        z.n[0] = B * K;
+        z.p[1] = reinterpret_cast<uint32_t*>(sp.bad);
+        z.n[1] = B;
+        const int64_t zb = min((B * K + kBlock - 1) / kBlock, (int64_t)4096);
+        hipLaunchKernelGGL(k_zero, dim3((unsigned)zb), dim3(kBlock), 0, s, z);
+        hipLaunchKernelGGL(k_histogram, tiles, dim3(kBlock), lds, s, sp.labels, sp.counts, sp.bad,
+                           N, K, use_lds);
+    }
+    const size_t plan_lds = (size_t)(3 * K + 2) * sizeof(int32_t);
+    const int plan_in_lds = plan_lds <= 60 * 1024;
+    int32_t* clear = sp.sums ? sp.clear : nullptr;
+    hipLaunchKernelGGL(k_plan, dim3((unsigned)B), dim3(kBlock), plan_in_lds ? plan_lds : 0, s,
+                       sp.counts, sp.offsets, sp.poff, sp.pieces, clear, sp.move, K, M,
+                       plan_in_lds);
+    if (tiled) {
+        hipLaunchKernelGGL(k_tile_scatter, tiles, dim3(kBlock), (size_t)K * sizeof(int32_t), s,
+                           sp.labels, sp.table, sp.offsets, sp.sorted_idx, clear, sp.sums,
+                           sp.arrive, N, K, T, M, sp.d);
+    } else {
+        const int64_t cb = min((K + kBlock - 1) / kBlock, (int64_t)256);
+        hipLaunchKernelGGL(k_cursor, dim3((unsigned)cb, (unsigned)B), dim3(kBlock), 0, s,
+                           sp.offsets, sp.table, K);
+        hipLaunchKernelGGL(k_scatter, tiles, dim3(kBlock), lds, s, sp.labels, sp.table,
+                           sp.sorted_idx, clear, sp.sums, sp.arrive, N, K, M, sp.d, use_lds);
+    }
     return hipGetLastError();
 }
 
