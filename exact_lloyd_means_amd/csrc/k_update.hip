@@ -314,10 +314,20 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(
     const int32_t* __restrict__ labels, const int32_t* __restrict__ th,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_idx,
     const int32_t* __restrict__ clear, float* __restrict__ sums, int32_t* __restrict__ arrive,
-    int64_t N, int64_t K, int64_t T, int64_t M, int64_t d) {
+    int64_t N, int64_t K, int64_t T, int64_t M, int64_t d, int xcd_map) {
     extern __shared__ int32_t s_base[];  // [K]
-    const int64_t b = blockIdx.y;
-    const int64_t t = blockIdx.x;
+    // Workgroups go to the 8 XCDs round-robin.  With xcd_map (B a multiple
+    // of 8, 1-D grid) all tiles of problem b run on XCD b mod 8, so the
+    // partial cache lines of its sorted indices merge in one L2.
+    int64_t b, t;
+    if (xcd_map) {
+        const int64_t x = blockIdx.x % 8, q = blockIdx.x / 8;
+        b = x + 8 * (q / T);
+        t = q % T;
+    } else {
+        b = blockIdx.y;
+        t = blockIdx.x;
+    }
     if (clear) clear_listed(clear + b * (M + 1), sums + b * K * d, arrive + b * K, d, t, T);
     const int32_t* pre = th + (b * T + t) * (K + 1);
     const int32_t* off = offsets + b * (K + 1);
@@ -867,9 +877,11 @@ hipError_t launch_sort(const SortParams& sp, int64_t B, int64_t N, int64_t K, hi
                        sp.counts, sp.offsets, sp.poff, sp.pieces, clear, sp.move, K, M,
                        plan_in_lds);
     if (tiled) {
-        hipLaunchKernelGGL(k_tile_scatter, tiles, dim3(kBlock), (size_t)K * sizeof(int32_t), s,
+        const int xcd_map = B % 8 == 0 && T * B < ((int64_t)1 << 31);
+        const dim3 sgrid = xcd_map ? dim3((unsigned)(T * B)) : tiles;
+        hipLaunchKernelGGL(k_tile_scatter, sgrid, dim3(kBlock), (size_t)K * sizeof(int32_t), s,
                            sp.labels, sp.table, sp.offsets, sp.sorted_idx, clear, sp.sums,
-                           sp.arrive, N, K, T, M, sp.d);
+                           sp.arrive, N, K, T, M, sp.d, xcd_map);
     } else {
         const int64_t cb = min((K + kBlock - 1) / kBlock, (int64_t)256);
         hipLaunchKernelGGL(k_cursor, dim3((unsigned)cb, (unsigned)B), dim3(kBlock), 0, s,
