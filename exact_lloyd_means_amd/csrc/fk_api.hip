@@ -44,8 +44,7 @@ Workspace workspace_layout(const fk_problem& p, char* base) {
     w.poff = reinterpret_cast<int32_t*>(take(B * (K + 1) * sizeof(int32_t)));
     w.pieces = reinterpret_cast<int32_t*>(
         take(B * (1 + 2 * (size_t)piece_capacity(p.N, p.K)) * sizeof(int32_t)));
-    w.clear = reinterpret_cast<int32_t*>(
-        take(B * (1 + (size_t)piece_capacity(p.N, p.K)) * sizeof(int32_t)));
+    w.part = reinterpret_cast<int32_t*>(take(B * 2 * (size_t)plan_blocks(p.K) * sizeof(int32_t)));
     w.sums = reinterpret_cast<float*>(take(B * K * d * sizeof(float)));
     w.arrive = reinterpret_cast<int32_t*>(take(B * K * sizeof(int32_t)));
     w.counts = reinterpret_cast<int32_t*>(take(B * K * sizeof(int32_t)));
@@ -78,6 +77,7 @@ StreamWorkspace stream_workspace_layout(const fk_problem& p, int64_t chunk, char
     w.poff = reinterpret_cast<int32_t*>(take((K + 1) * sizeof(int32_t)));
     w.pieces = reinterpret_cast<int32_t*>(
         take((1 + 2 * (size_t)piece_capacity(chunk, p.K)) * sizeof(int32_t)));
+    w.part = reinterpret_cast<int32_t*>(take(2 * (size_t)plan_blocks(p.K) * sizeof(int32_t)));
     w.bad = reinterpret_cast<int32_t*>(take(256));
     w.total = o;
     return w;
@@ -168,13 +168,13 @@ fk_status enqueue_sort(const fk_problem& p, const Workspace& w, const int32_t* l
     sp.sorted_idx = sorted_idx;
     sp.poff = w.poff;
     sp.pieces = w.pieces;
+    sp.part = w.part;
     sp.table = w.table;
     sp.bad = w.bad;
     sp.move = move;
     if (clear_update) {
         sp.sums = w.sums;
         sp.arrive = w.arrive;
-        sp.clear = w.clear;
         sp.d = p.d;
     }
     FK_TRY(launch_sort(sp, p.B, p.N, p.K, s), "sort labels");
@@ -421,6 +421,7 @@ fk_status fk_lloyd_streamed(const fk_problem* p, const void* X_host, int64_t chu
                     so.sorted_idx = w.sorted_idx;
                     so.poff = w.poff;
                     so.pieces = w.pieces;
+                    so.part = w.part;
                     so.table = w.table;
                     so.bad = w.bad;
                     FK_TRY(launch_sort(so, 1, n, K, cs), "sort chunk labels");

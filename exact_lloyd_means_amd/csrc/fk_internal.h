@@ -24,6 +24,9 @@ inline int dtype_size(int dtype) { return dtype == FK_F32 ? 4 : 2; }
 constexpr int kSegRun = 256;
 // Pieces a problem can have: sum over segments of ceil(count / kSegRun).
 inline int64_t piece_capacity(int64_t N, int64_t K) { return (N + kSegRun - 1) / kSegRun + K; }
+// Labels per workgroup of the plan (offsets and pieces) and blocks per problem.
+constexpr int64_t kPlanLabels = 4096;
+inline int64_t plan_blocks(int64_t K) { return (K + kPlanLabels - 1) / kPlanLabels; }
 
 // Counting sort plan: the tiled form (per-tile count table, no global
 // atomics) when K is small enough for LDS bins and the table stays modest.
@@ -41,7 +44,7 @@ struct Workspace {
     int32_t* sorted_idx; // [B][N]   argsort of the labels
     int32_t* poff;       // [B][K+1] first piece of each segment
     int32_t* pieces;     // [B][1 + 2 * piece_capacity] piece count, segments, starts
-    int32_t* clear;      // [B][1 + piece_capacity] segments whose sum rows to clear
+    int32_t* part;       // [B][2 * plan_blocks(K)] block totals of the plan
     float* sums;         // [B][K][d] fp32 segment sums
     int32_t* arrive;     // [B][K]   pieces of each segment added so far
     int32_t* counts;     // [B][K]   counts when the caller passes none
@@ -66,6 +69,7 @@ struct StreamWorkspace {
     int32_t* sorted_idx; // [chunk]
     int32_t* poff;       // [K+1]
     int32_t* pieces;     // [1 + 2 * piece_capacity(chunk)]
+    int32_t* part;       // [2 * plan_blocks(K)]
     int32_t* bad;        // [1]
     size_t total;
 };
@@ -85,7 +89,7 @@ struct SortParams {
     uint32_t* move;         // cleared when not null
     float* sums;            // [B][K][d] rows of multi-piece segments cleared (or null)
     int32_t* arrive;        // [B][K]   their arrival counters cleared
-    int32_t* clear;         // [B][1 + piece_capacity] list of those segments
+    int32_t* part;          // [B][2 * plan_blocks(K)] block totals of the plan
     int64_t d;
 };
 

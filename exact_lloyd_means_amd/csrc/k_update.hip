@@ -123,78 +123,57 @@ __global__ __launch_bounds__(kBlock) void k_prepare(const float* __restrict__ C,
 // cut into pieces of at most kSegRun sorted positions, one wave each.  The
 // piece block of a problem holds P[0] = number of pieces, P[1 + j] = the
 // segment of piece j and P[1 + M + j] = its first position (M = capacity);
-// poff[k] is the first piece of segment k.  Segments of several pieces are
-// the only ones the segment sums accumulate into; when clear is not null
-// they are listed there (clear[0] = n, clear[1..n] = segments) so the next
-// kernel can clear their sum rows and arrival counters.  Thread-strided over
-// k; off may live in LDS or global memory.
-__device__ inline void write_pieces(const int32_t* off, const int32_t* __restrict__ poff,
-                                    int64_t K, int32_t* __restrict__ P, int64_t M,
-                                    int32_t* __restrict__ clear) {
-    __shared__ int32_t s_n;
-    if (threadIdx.x == 0) s_n = 0;
-    __syncthreads();
-    for (int64_t k = threadIdx.x; k < K; k += blockDim.x) {
-        const int32_t s = off[k], e = off[k + 1];
-        int64_t j = poff[k];
-        for (int32_t p = s; p < e; p += kSegRun, ++j) {
-            P[1 + j] = (int32_t)k;
-            P[1 + M + j] = p;
-        }
-        if (clear && e - s > kSegRun) clear[1 + atomicAdd(&s_n, 1)] = (int32_t)k;
-    }
-    if (threadIdx.x == 0) P[0] = poff[K];
-    __syncthreads();
-    if (clear && threadIdx.x == 0) clear[0] = s_n;
-}
+// poff[k] is the first piece of segment k.
+__device__ inline int32_t npieces_of(int32_t count) { return (count + kSegRun - 1) / kSegRun; }
 
-// Clears the sum rows and arrival counters listed by write_pieces: this
-// workgroup's share, one wave per row.
-__device__ inline void clear_listed(const int32_t* __restrict__ clear, float* __restrict__ sums,
-                                    int32_t* __restrict__ arrive, int64_t d, int64_t wg,
-                                    int64_t nwg) {
-    const int n = clear[0];
+// Clears the sum rows and arrival counters of the segments with more than
+// one piece (the only rows the segment sums accumulate into): workgroup wg
+// of nwg takes every nwg-th group of rows, one wave per row.
+__device__ inline void clear_multi_rows(const int32_t* __restrict__ counts,
+                                        float* __restrict__ sums, int32_t* __restrict__ arrive,
+                                        int64_t K, int64_t d, int64_t wg, int64_t nwg) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int nw = blockDim.x / kWave;
-    for (int64_t r = wg * nw + threadIdx.x / kWave; r < n; r += nwg * nw) {
-        const int32_t k = clear[1 + r];
-        float* row = sums + (int64_t)k * d;
+    const int64_t nw = blockDim.x / kWave;
+    for (int64_t k = wg * nw + threadIdx.x / kWave; k < K; k += nwg * nw) {
+        if (counts[k] <= kSegRun) continue;
+        float* row = sums + k * d;
         for (int64_t c = lane; c < d; c += kWave) row[c] = 0.f;
         if (lane == 0) arrive[k] = 0;
     }
 }
 
-// Block-wide exclusive scan of counts[0..K) into off[0..K] (LDS or global,
-// off[K] = total); with PIECES the scanned value of label k is its number
-// of pieces, ceil(counts[k] / kSegRun).  Each thread owns a contiguous range
-// of labels.
-template <bool PIECES>
-__device__ inline void block_offsets(const int32_t* __restrict__ counts, int64_t K,
-                                     int32_t* __restrict__ off, int32_t* __restrict__ s_part) {
-    auto val = [&](int64_t k) -> int32_t {
-        const int32_t c = counts[k];
-        return PIECES ? (c + kSegRun - 1) / kSegRun : c;
-    };
-    const int64_t per = (K + kBlock - 1) / kBlock;
-    const int64_t k0 = min((int64_t)threadIdx.x * per, K);
-    const int64_t k1 = min(k0 + per, K);
+// Exclusive scan of v[0..n) in LDS (n <= kBlock * kPlanPer), in place, by
+// one workgroup; returns the total.  Each thread owns kPlanPer consecutive
+// entries.
+constexpr int kPlanPer = 16;
+constexpr int kPlanBlock = kBlock * kPlanPer;  // labels per plan workgroup
+static_assert(kPlanBlock == kPlanLabels, "plan block size");
+__device__ inline int32_t lds_exclusive_scan(int32_t* __restrict__ v, int n,
+                                             int32_t* __restrict__ s_part) {
+    const int i0 = threadIdx.x * kPlanPer;
     int32_t local = 0;
-    for (int64_t k = k0; k < k1; ++k) local += val(k);
+#pragma unroll
+    for (int u = 0; u < kPlanPer; ++u) local += i0 + u < n ? v[i0 + u] : 0;
     s_part[threadIdx.x] = local;
     __syncthreads();
     for (int o = 1; o < kBlock; o <<= 1) {
-        const int32_t v = threadIdx.x >= o ? s_part[threadIdx.x - o] : 0;
+        const int32_t t = threadIdx.x >= o ? s_part[threadIdx.x - o] : 0;
         __syncthreads();
-        s_part[threadIdx.x] += v;
+        s_part[threadIdx.x] += t;
         __syncthreads();
     }
     int32_t run = s_part[threadIdx.x] - local;
-    for (int64_t k = k0; k < k1; ++k) {
-        off[k] = run;
-        run += val(k);
+#pragma unroll
+    for (int u = 0; u < kPlanPer; ++u) {
+        if (i0 + u < n) {
+            const int32_t x = v[i0 + u];
+            v[i0 + u] = run;
+            run += x;
+        }
     }
-    if (threadIdx.x == kBlock - 1) off[K] = s_part[kBlock - 1];
+    const int32_t total = s_part[kBlock - 1];
     __syncthreads();
+    return total;
 }
 
 // ---- tiled counting sort ----------------------------------------------------
@@ -235,18 +214,46 @@ __global__ __launch_bounds__(kBlock) void k_tile_hist(const int32_t* __restrict_
 }
 
 // Column pass: th[b][t][k] <- sum_{t' < t} th[b][t'][k]; counts[b][k] and
-// bad[b] (column K) receive the column totals.
+// bad[b] (column K) receive the column totals.  A workgroup takes 64
+// columns; the 4 waves split the tiles into 4 consecutive groups, sum their
+// group, exchange the group totals through LDS and rewrite their group as a
+// running prefix.
+constexpr int kColGroups = kBlock / kWave;
 __global__ __launch_bounds__(kBlock) void k_tile_colscan(int32_t* __restrict__ th,
                                                          int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ bad, int64_t K,
                                                          int64_t T) {
+    __shared__ int32_t s_tot[kColGroups][kWave];
     const int64_t b = blockIdx.y;
-    const int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int g = threadIdx.x / kWave;
+    const int64_t k = (int64_t)blockIdx.x * kWave + lane;
+    const int64_t per = (T + kColGroups - 1) / kColGroups;
+    const int64_t t0 = min(g * per, T), t1 = min(t0 + per, T);
+    int32_t* col = th + b * T * (K + 1) + min(k, K);
+    int32_t sum = 0;
+    if (k <= K) {
+        int64_t t = t0;
+        for (; t + 8 <= t1; t += 8) {
+            int32_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = col[(t + u) * (K + 1)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) sum += v[u];
+        }
+        for (; t < t1; ++t) sum += col[t * (K + 1)];
+    }
+    s_tot[g][lane] = sum;
+    __syncthreads();
+    int32_t run = 0, total = 0;
+#pragma unroll
+    for (int q = 0; q < kColGroups; ++q) {
+        run += q < g ? s_tot[q][lane] : 0;
+        total += s_tot[q][lane];
+    }
     if (k > K) return;
-    int32_t* col = th + b * T * (K + 1) + k;
-    int32_t run = 0;
-    int64_t t = 0;
-    for (; t + 8 <= T; t += 8) {
+    int64_t t = t0;
+    for (; t + 8 <= t1; t += 8) {
         int32_t v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) v[u] = col[(t + u) * (K + 1)];
@@ -256,65 +263,137 @@ __global__ __launch_bounds__(kBlock) void k_tile_colscan(int32_t* __restrict__ t
             run += v[u];
         }
     }
-    for (; t < T; ++t) {
+    for (; t < t1; ++t) {
         const int32_t v = col[t * (K + 1)];
         col[t * (K + 1)] = run;
         run += v;
     }
-    if (k < K)
-        counts[b * K + k] = run;
-    else
-        bad[b] = run;
+    if (g == 0) {
+        if (k < K)
+            counts[b * K + k] = total;
+        else
+            bad[b] = total;
+    }
 }
 
-// Plan of one problem (one workgroup each): offsets = exclusive scan of the
-// counts, the pieces of the segment sums and the list of sum rows to clear;
-// problem 0 clears the move word.
-// With use_lds the counts and both scans live in LDS (3K + 2 words), so the
-// dependent steps wait on LDS rather than on global memory.
+// Plan, part 1 (only when K > kPlanBlock): totals of counts and pieces of
+// every block of kPlanBlock labels.
+__global__ __launch_bounds__(kBlock) void k_plan_totals(const int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ part, int64_t K) {
+    __shared__ int32_t s_red[2][kBlock];
+    const int64_t b = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
+    const int64_t k0 = blk * kPlanBlock;
+    int32_t c = 0, p = 0;
+    for (int64_t k = k0 + threadIdx.x; k < min(k0 + kPlanBlock, K); k += kBlock) {
+        const int32_t v = counts[b * K + k];
+        c += v;
+        p += npieces_of(v);
+    }
+    s_red[0][threadIdx.x] = c;
+    s_red[1][threadIdx.x] = p;
+    __syncthreads();
+    for (int o = kBlock / 2; o > 0; o >>= 1) {
+        if (threadIdx.x < o) {
+            s_red[0][threadIdx.x] += s_red[0][threadIdx.x + o];
+            s_red[1][threadIdx.x] += s_red[1][threadIdx.x + o];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        part[(b * nblk + blk) * 2 + 0] = s_red[0][0];
+        part[(b * nblk + blk) * 2 + 1] = s_red[1][0];
+    }
+}
+
+// Plan, part 2: for block blk of kPlanBlock labels of problem b, the
+// offsets (exclusive scan of the counts) and first pieces, then every piece
+// of the block's segments, written in parallel over pieces (a binary search
+// over the block's first pieces finds the segment).  The last block writes
+// the totals; block 0 of problem 0 clears the move word.
 __global__ __launch_bounds__(kBlock) void k_plan(const int32_t* __restrict__ counts,
+                                                 const int32_t* __restrict__ part,
                                                  int32_t* __restrict__ offsets,
                                                  int32_t* __restrict__ poff,
                                                  int32_t* __restrict__ pieces,
-                                                 int32_t* __restrict__ clear,
                                                  uint32_t* __restrict__ move, int64_t K,
-                                                 int64_t M, int use_lds) {
+                                                 int64_t M) {
+    __shared__ int32_t s_off[kPlanBlock];
+    __shared__ int32_t s_po[kPlanBlock];
     __shared__ int32_t s_part[kBlock];
-    extern __shared__ int32_t s_plan[];
-    const int64_t b = blockIdx.x;
+    __shared__ int32_t s_base[2];
+    const int64_t b = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
+    const int64_t k0 = blk * kPlanBlock;
+    const int n = (int)min((int64_t)kPlanBlock, K - k0);
+    if (threadIdx.x < 2) {
+        int32_t acc = 0;
+        for (int64_t q = 0; q < blk; ++q) acc += part[(b * nblk + q) * 2 + threadIdx.x];
+        s_base[threadIdx.x] = acc;
+    }
+    for (int i = threadIdx.x; i < n; i += kBlock) {
+        const int32_t v = counts[b * K + k0 + i];
+        s_off[i] = v;
+        s_po[i] = npieces_of(v);
+    }
+    __syncthreads();
+    const int32_t tot_c = lds_exclusive_scan(s_off, n, s_part);
+    const int32_t tot_p = lds_exclusive_scan(s_po, n, s_part);
+    const int32_t bc = s_base[0], bp = s_base[1];
     int32_t* off = offsets + b * (K + 1);
     int32_t* po = poff + b * (K + 1);
-    const int32_t* cnt = counts + b * K;
-    int32_t* l_off = off;
-    int32_t* l_po = po;
-    if (use_lds) {
-        int32_t* l_cnt = s_plan;
-        l_off = s_plan + K;
-        l_po = s_plan + 2 * K + 1;
-        for (int64_t k = threadIdx.x; k < K; k += kBlock) l_cnt[k] = cnt[k];
-        __syncthreads();
-        cnt = l_cnt;
+    for (int i = threadIdx.x; i < n; i += kBlock) {
+        off[k0 + i] = bc + s_off[i];
+        po[k0 + i] = bp + s_po[i];
     }
-    block_offsets<false>(cnt, K, l_off, s_part);
-    block_offsets<true>(cnt, K, l_po, s_part);
-    write_pieces(l_off, l_po, K, pieces + b * (2 * M + 1), M, clear ? clear + b * (M + 1) : nullptr);
-    if (use_lds) {
-        for (int64_t k = threadIdx.x; k <= K; k += kBlock) {
-            off[k] = l_off[k];
-            po[k] = l_po[k];
+    int32_t* P = pieces + b * (2 * M + 1);
+    if (blk == nblk - 1 && threadIdx.x == 0) {
+        off[K] = bc + tot_c;
+        po[K] = bp + tot_p;
+        P[0] = bp + tot_p;
+    }
+    // pieces of this block: a segment of few pieces is written by the thread
+    // that owns it; segments of many pieces (hot clusters) are listed and
+    // written by the whole workgroup
+    __shared__ int32_t s_big[kBlock];
+    __shared__ int32_t s_nbig;
+    if (threadIdx.x == 0) s_nbig = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += kBlock) {
+        const int32_t pc = (i + 1 < n ? s_po[i + 1] : tot_p) - s_po[i];
+        if (pc > 8) {
+            const int32_t at = atomicAdd(&s_nbig, 1);
+            if (at < kBlock) {
+                s_big[at] = i;
+                continue;
+            }
+        }
+        for (int32_t q = 0; q < pc; ++q) {
+            const int64_t j = bp + s_po[i] + q;
+            P[1 + j] = (int32_t)(k0 + i);
+            P[1 + M + j] = bc + s_off[i] + q * kSegRun;
         }
     }
-    if (b == 0 && threadIdx.x == 0 && move) *move = 0u;
+    __syncthreads();
+    const int nbig = min(s_nbig, kBlock);
+    for (int r = 0; r < nbig; ++r) {
+        const int i = s_big[r];
+        const int32_t pc = (i + 1 < n ? s_po[i + 1] : tot_p) - s_po[i];
+        for (int32_t q = threadIdx.x; q < pc; q += kBlock) {
+            const int64_t j = bp + s_po[i] + q;
+            P[1 + j] = (int32_t)(k0 + i);
+            P[1 + M + j] = bc + s_off[i] + q * kSegRun;
+        }
+    }
+    if (b == 0 && blk == 0 && threadIdx.x == 0 && move) *move = 0u;
 }
 
 // Scatter of tile t: base of label k = offsets[k] + th[b][t][k]; elements
-// are ranked with LDS atomics.  The workgroups also clear the listed sum
-// rows (clear may be null).
+// are ranked with LDS atomics.  With sums the workgroups also clear the sum
+// rows of multi-piece segments.
 __global__ __launch_bounds__(kBlock) void k_tile_scatter(
     const int32_t* __restrict__ labels, const int32_t* __restrict__ th,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_idx,
-    const int32_t* __restrict__ clear, float* __restrict__ sums, int32_t* __restrict__ arrive,
-    int64_t N, int64_t K, int64_t T, int64_t M, int64_t d, int xcd_map) {
+    const int32_t* __restrict__ counts, float* __restrict__ sums, int32_t* __restrict__ arrive,
+    int64_t N, int64_t K, int64_t T, int64_t d, int xcd_map) {
     extern __shared__ int32_t s_base[];  // [K]
     // Workgroups go to the 8 XCDs round-robin.  With xcd_map (B a multiple
     // of 8, 1-D grid) all tiles of problem b run on XCD b mod 8, so the
@@ -328,7 +407,7 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(
         b = blockIdx.y;
         t = blockIdx.x;
     }
-    if (clear) clear_listed(clear + b * (M + 1), sums + b * K * d, arrive + b * K, d, t, T);
+    if (sums) clear_multi_rows(counts + b * K, sums + b * K * d, arrive + b * K, K, d, t, T);
     const int32_t* pre = th + (b * T + t) * (K + 1);
     const int32_t* off = offsets + b * (K + 1);
     for (int64_t k = threadIdx.x; k < K; k += kBlock) s_base[k] = off[k] + pre[k];
@@ -404,15 +483,15 @@ __global__ void k_cursor(const int32_t* __restrict__ offsets, int32_t* __restric
 __global__ __launch_bounds__(kBlock) void k_scatter(const int32_t* __restrict__ labels,
                                                     int32_t* __restrict__ cursor,
                                                     int32_t* __restrict__ sorted_idx,
-                                                    const int32_t* __restrict__ clear,
+                                                    const int32_t* __restrict__ counts,
                                                     float* __restrict__ sums,
                                                     int32_t* __restrict__ arrive, int64_t N,
-                                                    int64_t K, int64_t M, int64_t d, int use_lds) {
+                                                    int64_t K, int64_t d, int use_lds) {
     extern __shared__ int32_t s_base[];
     const int64_t b = blockIdx.y;
-    if (clear)
-        clear_listed(clear + b * (M + 1), sums + b * K * d, arrive + b * K, d, blockIdx.x,
-                     gridDim.x);
+    if (sums)
+        clear_multi_rows(counts + b * K, sums + b * K * d, arrive + b * K, K, d, blockIdx.x,
+                         gridDim.x);
     const int64_t i0 = (int64_t)blockIdx.x * kSortTile;
     const int64_t i1 = min(i0 + (int64_t)kSortTile, N);
     const int32_t* lab = labels + b * N;
@@ -561,13 +640,15 @@ __device__ inline void finalize_row(const SegOut<T>& o, int64_t b, int64_t K, in
 // piece adds its sums with one row of fp32 atomics, and with FINAL the last
 // piece to arrive finalizes the segment.  Extra workgroups past the pieces
 // (FINAL only) give empty segments their previous centroid.
-// VEC: rows load through a buffer resource (d % EPL == 0 and the problem's
-// rows span less than 2 GiB); otherwise element by element with bounds.
-template <typename T, int EPL, bool VEC, bool FINAL>
+// LD = 2: rows load through a buffer resource (d % EPL == 0 and the
+// problem's rows span less than 2 GiB); LD = 1: whole parts with 64-bit
+// addresses (d % EPL == 0); LD = 0: element by element with bounds.
+template <typename T, int EPL, int LD, bool FINAL>
 __global__ __launch_bounds__(kBlock) void k_segment_sums(
     const T* __restrict__ X, const int32_t* __restrict__ sorted_idx,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ pieces, SegOut<T> o,
     int64_t N, int64_t K, int d, int64_t M, int64_t piece_wgs) {
+    constexpr bool VEC = LD != 0;
     constexpr int RB = seg_batch<T, EPL>();
     constexpr int NV = kSegRun / kWave;  // index registers per lane
     const int lane = threadIdx.x & 63;
@@ -613,7 +694,7 @@ __global__ __launch_bounds__(kBlock) void k_segment_sums(
     const int n = min(kSegRun, s1 - p0);  // rows of this piece
     const T* __restrict__ Xb = X + b * N * d;
     __amdgpu_buffer_rsrc_t rsrc;
-    if constexpr (VEC)
+    if constexpr (LD == 2)
         rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(Xb), 0,
                                                  (int32_t)(N * d * (int64_t)sizeof(T)), 0x00020000);
     const int32_t rowb = d * (int32_t)sizeof(T);
@@ -637,10 +718,10 @@ __global__ __launch_bounds__(kBlock) void k_segment_sums(
             for (int u = 0; u < RB; ++u) {
                 const int pos = base + u;
                 const int32_t row = __builtin_amdgcn_readlane(vidx[pos / kWave], pos % kWave);
-                if constexpr (VEC)
+                if constexpr (LD == 2)
                     v[u] = load_row_part_buf<T, EPL>(rsrc, row * rowb, lane_off);
                 else
-                    v[u] = load_row_part<T, EPL, false>(Xb, row, d, active ? e0 : 0);
+                    v[u] = load_row_part<T, EPL, VEC>(Xb, row, d, active ? e0 : 0);
             }
             if (active) {
                 if (base + RB <= n) {
@@ -765,13 +846,15 @@ hipError_t segment_sums_t(const void* X, const int32_t* sorted_idx, const int32_
     const bool buf_ok = N * (int64_t)d * (int64_t)sizeof(T) < ((int64_t)1 << 31);
 #define FK_SEG_CASE(E)                                                                         \
     if (epl <= E) {                                                                            \
-        const bool vec = d % E == 0 && buf_ok;                                                 \
+        const int ld = d % E != 0 ? 0 : (buf_ok ? 2 : 1);                                      \
         if (sp.final) {                                                                        \
-            if (vec) FK_SEG_LAUNCH(E, true, true);                                             \
-            else FK_SEG_LAUNCH(E, false, true);                                                \
+            if (ld == 2) FK_SEG_LAUNCH(E, 2, true);                                            \
+            else if (ld == 1) FK_SEG_LAUNCH(E, 1, true);                                       \
+            else FK_SEG_LAUNCH(E, 0, true);                                                    \
         } else {                                                                               \
-            if (vec) FK_SEG_LAUNCH(E, true, false);                                            \
-            else FK_SEG_LAUNCH(E, false, false);                                               \
+            if (ld == 2) FK_SEG_LAUNCH(E, 2, false);                                           \
+            else if (ld == 1) FK_SEG_LAUNCH(E, 1, false);                                      \
+            else FK_SEG_LAUNCH(E, 0, false);                                                   \
         }                                                                                      \
         return hipGetLastError();                                                              \
     }
@@ -857,7 +940,7 @@ hipError_t launch_sort(const SortParams& sp, int64_t B, int64_t N, int64_t K, hi
     if (tiled) {
         hipLaunchKernelGGL(k_tile_hist, tiles, dim3(kBlock), (size_t)(K + 1) * sizeof(int32_t), s,
                            sp.labels, sp.table, N, K, T);
-        hipLaunchKernelGGL(k_tile_colscan, dim3((unsigned)((K + kBlock) / kBlock), (unsigned)B),
+        hipLaunchKernelGGL(k_tile_colscan, dim3((unsigned)((K + kWave) / kWave), (unsigned)B),
                            dim3(kBlock), 0, s, sp.table, sp.counts, sp.bad, K, T);
     } else {
         ZeroRanges z{};
@@ -870,24 +953,24 @@ hipError_t launch_sort(const SortParams& sp, int64_t B, int64_t N, int64_t K, hi
         hipLaunchKernelGGL(k_histogram, tiles, dim3(kBlock), lds, s, sp.labels, sp.counts, sp.bad,
                            N, K, use_lds);
     }
-    const size_t plan_lds = (size_t)(3 * K + 2) * sizeof(int32_t);
-    const int plan_in_lds = plan_lds <= 60 * 1024;
-    int32_t* clear = sp.sums ? sp.clear : nullptr;
-    hipLaunchKernelGGL(k_plan, dim3((unsigned)B), dim3(kBlock), plan_in_lds ? plan_lds : 0, s,
-                       sp.counts, sp.offsets, sp.poff, sp.pieces, clear, sp.move, K, M,
-                       plan_in_lds);
+    const int64_t nblk = (K + kPlanBlock - 1) / kPlanBlock;
+    if (nblk > 1)
+        hipLaunchKernelGGL(k_plan_totals, dim3((unsigned)nblk, (unsigned)B), dim3(kBlock), 0, s,
+                           sp.counts, sp.part, K);
+    hipLaunchKernelGGL(k_plan, dim3((unsigned)nblk, (unsigned)B), dim3(kBlock), 0, s, sp.counts,
+                       sp.part, sp.offsets, sp.poff, sp.pieces, sp.move, K, M);
     if (tiled) {
         const int xcd_map = B % 8 == 0 && T * B < ((int64_t)1 << 31);
         const dim3 sgrid = xcd_map ? dim3((unsigned)(T * B)) : tiles;
         hipLaunchKernelGGL(k_tile_scatter, sgrid, dim3(kBlock), (size_t)K * sizeof(int32_t), s,
-                           sp.labels, sp.table, sp.offsets, sp.sorted_idx, clear, sp.sums,
-                           sp.arrive, N, K, T, M, sp.d, xcd_map);
+                           sp.labels, sp.table, sp.offsets, sp.sorted_idx, sp.counts, sp.sums,
+                           sp.arrive, N, K, T, sp.d, xcd_map);
     } else {
         const int64_t cb = min((K + kBlock - 1) / kBlock, (int64_t)256);
         hipLaunchKernelGGL(k_cursor, dim3((unsigned)cb, (unsigned)B), dim3(kBlock), 0, s,
                            sp.offsets, sp.table, K);
         hipLaunchKernelGGL(k_scatter, tiles, dim3(kBlock), lds, s, sp.labels, sp.table,
-                           sp.sorted_idx, clear, sp.sums, sp.arrive, N, K, M, sp.d, use_lds);
+                           sp.sorted_idx, sp.counts, sp.sums, sp.arrive, N, K, sp.d, use_lds);
     }
     return hipGetLastError();
 }
