@@ -1,0 +1,389 @@
+// k_assign16.inl -- fused distance + running argmin for 16-bit inputs on
+// the 16x16x32 matrix instructions.
+//
+// Same method and pipeline as k_assign.inl (papernotes.org notes
+// "Flash-KMeans: Fast and Memory-Efficient Exact K-Means", 关键设计 1: never
+// store the N x K distance matrix, keep a running (min, argmin) per point),
+// with v_mfma_f32_16x16x32_{f16,bf16} in place of the 32x32x16 form.  Under
+// full load the MI355X matrix units are power-limited; with random operands
+// the 16x16x32 form (a quarter of the accumulator registers per instruction)
+// sustains markedly more flops than the 32x32x16 form, so it is used for the
+// 16-bit types.
+//
+// Lane layout of v_mfma_f32_16x16x32: lane l supplies A[l%16][8*(l/16) + j]
+// and B[8*(l/16) + j][l%16] (j = 0..7) and holds D[4*(l/16) + i][l%16]
+// (i = 0..3).  Rows are centroids, columns points: each point's 16 scores of
+// a 16-centroid block are spread over the four lanes l%16 + 16*g, four each,
+// and the four lanes merge once at the end.
+#pragma once
+
+#include "k_assign.inl"
+
+namespace fk {
+namespace {
+
+template <typename T>
+struct Mfma16;
+
+template <>
+struct Mfma16<_Float16> {
+    __device__ static inline floatx4 step(u32x4 a, u32x4 b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
+                                                      __builtin_bit_cast(half8, b), c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Mfma16<__bf16> {
+    __device__ static inline floatx4 step(u32x4 a, u32x4 b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+
+// S = k-steps of 32 dimensions (d <= 32 S), NP = 16-point column blocks held
+// by each wave, VEC / EXACT / SMALLK as in k_assign.
+//
+// Tile of 32 centroids = 2 row blocks of 16.  A slot is the NP MFMAs that
+// share one centroid fragment (row block rb, k-step s), slot order s-major;
+// each slot is preceded by the epilogue of one row (rb, i) of tile t for all
+// NP point blocks.  Staging (registers -> ring of four LDS buffers), the
+// prefetch of the next tile's fragments and bias, and the branch-free
+// overlapping last tile are those of k_assign.
+template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK>
+__global__ __launch_bounds__(kAssignWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_assign16(const T* __restrict__ X, const T* __restrict__ C, const float* __restrict__ bias,
+                int32_t* __restrict__ labels, float* __restrict__ min_dist, int64_t B, int64_t N,
+                int64_t K, int d) {
+    using M = Mfma16<T>;
+    using MS = Mfma<T>;
+    constexpr int V = 8;                               // elements per 16-byte chunk
+    constexpr int RC = 4 * S;                          // 16-byte chunks per row
+    constexpr int ROWB = RC * 16 + 16;                 // LDS bytes per centroid row (padded)
+    constexpr int TILEB = kAssignBK * ROWB;
+    constexpr int CHUNKS = kAssignBK * RC;             // 16-byte chunks per centroid tile
+    constexpr int NT = kAssignWaves * kWave;
+    constexpr int PER = (CHUNKS + NT - 1) / NT;
+    constexpr int PTS = kAssignWaves * NP * 16;        // points per item
+    constexpr int RB = 2;                              // row blocks per tile
+    constexpr int kSlots = S * RB;
+    constexpr int P = kSlots <= 2 ? kSlots : 2;        // fragments prefetched for the next tile
+    constexpr int kBiasSlot = kSlots > 3 ? kSlots - 3 : 0;
+    static_assert(!EXACT || VEC, "EXACT implies VEC");
+
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    char* s_tile = smem;                                                      // [ring][TILEB]
+    float* s_bias = reinterpret_cast<float*>(smem + kAssignRing * TILEB);     // [ring][BK]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4;     // k group of the fragments, row group of the scores
+    const int col = lane & 15;
+    const int K32 = (int)K;
+    const int ntiles = (int)((K + kAssignBK - 1) / kAssignBK);
+    const int lastbase = SMALLK ? 0 : K32 - kAssignBK;
+    const int64_t nbpp = (N + PTS - 1) / PTS;
+    const int64_t items = B * nbpp;
+
+    int crow[PER], ccol[PER];
+    uint32_t goff[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int c = tid + u * NT;
+        crow[u] = c / RC;
+        ccol[u] = c % RC;
+        const int cofs = EXACT ? ccol[u] * V : min(ccol[u] * V, d - V);
+        goff[u] = (uint32_t)((crow[u] * d + cofs) * (int)sizeof(T));
+    }
+    auto tile_base = [&](int t) { return SMALLK ? 0 : min(t * kAssignBK, lastbase); };
+    struct Staged {
+        u32x4 v[PER];
+        float bias;
+    };
+
+    float best[NP];
+    int32_t bidx[NP];
+    u32x4 xf[NP][S];
+
+    for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+        const int64_t b = item / nbpp;
+        const int64_t pbase = (item - b * nbpp) * PTS + (int64_t)wave * NP * 16;
+        const T* __restrict__ Cb = C + b * K * d;
+        const float* __restrict__ biasb = bias + b * K;
+
+        // ---- this item's points, resident in registers for the K loop:
+        // k-step s of point column col holds dimensions 32 s + 8 g .. + 7
+#pragma unroll
+        for (int np = 0; np < NP; ++np) {
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+                xf[np][s] = load_chunk<T, VEC>(X + b * N * d, pbase + np * 16 + col, N, d,
+                                               32 * s + 8 * g);
+            best[np] = -INFINITY;
+            bidx[np] = 0;
+        }
+
+        auto gload = [&](int t, Staged& st) {
+            const int tbase = tile_base(t);
+            const char* base = reinterpret_cast<const char*>(Cb + (int64_t)tbase * d);
+#pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                if (CHUNKS % NT == 0 || u * NT + tid < CHUNKS) {
+                    if constexpr (SMALLK || !VEC) {
+                        st.v[u] = load_chunk<T, VEC>(Cb, tbase + crow[u], K, d, ccol[u] * V);
+                    } else {
+                        st.v[u] = *reinterpret_cast<const u32x4*>(base + goff[u]);
+                    }
+                }
+            }
+            if constexpr (SMALLK) {
+                const int k = tid & (kAssignBK - 1);
+                const float v = biasb[min(k, K32 - 1)];
+                st.bias = k < K32 ? v : -INFINITY;
+            } else {
+                st.bias = biasb[tbase + (tid & (kAssignBK - 1))];
+            }
+        };
+        auto sstore = [&](int buf, const Staged& st) {
+#pragma unroll
+            for (int u = 0; u < PER; ++u)
+                if (CHUNKS % NT == 0 || u * NT + tid < CHUNKS)
+                    *reinterpret_cast<u32x4*>(s_tile + buf * TILEB + crow[u] * ROWB +
+                                              ccol[u] * 16) = st.v[u];
+            s_bias[buf * kAssignBK + (tid & (kAssignBK - 1))] = st.bias;
+        };
+        // fragment of slot sl (k-step sl / RB, row block sl % RB) of the tile
+        // in LDS buffer buf: row 16 rb + col, chunk 4 s + g
+        auto frag = [&](int buf, int sl) -> u32x4 {
+            const int s = sl / RB, rb = sl % RB;
+            return *reinterpret_cast<const u32x4*>(s_tile + buf * TILEB + (16 * rb + col) * ROWB +
+                                                   (4 * s + g) * 16);
+        };
+        // bias of this lane's accumulator rows 16 rb + 4 g + i
+        auto bias_vec = [&](int buf, floatx4 (&bv)[RB]) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                bv[rb] = *reinterpret_cast<const floatx4*>(s_bias + buf * kAssignBK + 16 * rb + 4 * g);
+        };
+
+        // Running (max score, lowest index) per point block; within a tile
+        // the candidate index is the row offset 16 rb + i of the lane's row
+        // group (an inline constant, -1 = no improvement in this tile); rows
+        // ascend with (rb, i), so strict > keeps the lowest index.
+        float m[NP];
+        int32_t rt[NP];
+        auto epi_begin = [&]() {
+#pragma unroll
+            for (int np = 0; np < NP; ++np) {
+                m[np] = best[np];
+                rt[np] = -1;
+            }
+        };
+        // row r = 4 rb + i of all point blocks
+        auto epi_row = [&](const floatx4 (&sc)[RB][NP], int r) {
+            const int rb = r >> 2, i = r & 3;
+#pragma unroll
+            for (int np = 0; np < NP; ++np) {
+                const float s = sc[rb][np][i];
+                const bool keep = !(s > m[np]);
+                m[np] = keep ? m[np] : s;
+                rt[np] = keep ? rt[np] : 16 * rb + i;
+            }
+        };
+        auto epi_end = [&](int t) {
+            const int32_t kb = tile_base(t);
+#pragma unroll
+            for (int np = 0; np < NP; ++np) {
+                best[np] = m[np];
+                bidx[np] = rt[np] >= 0 ? kb + rt[np] : bidx[np];
+            }
+        };
+
+        floatx4 acc[2][RB][NP];
+        Staged st[2];
+        u32x4 a[kSlots];  // centroid fragments of the tile whose MFMAs run next
+        floatx4 bv[RB];   // and its bias
+
+        // ---- prologue: tiles 0, 1, 2 into LDS, tile 3 staged; tile 0's
+        // MFMAs; tile 1's first fragments and bias prefetched
+        gload(0, st[0]);
+        gload(1, st[1]);
+        sstore(0, st[0]);
+        sstore(1, st[1]);
+        gload(2, st[0]);
+        gload(3, st[1]);
+        sstore(2, st[0]);
+        __syncthreads();
+        bias_vec(0, bv);
+#pragma unroll
+        for (int sl = 0; sl < kSlots; ++sl) {
+            const u32x4 f = frag(0, sl);
+            const int s = sl / RB, rb = sl % RB;
+#pragma unroll
+            for (int np = 0; np < NP; ++np)
+                acc[0][rb][np] = M::step(f, xf[np][s], s == 0 ? bv[rb] : acc[0][rb][np]);
+        }
+#pragma unroll
+        for (int q = 0; q < P; ++q) a[q] = frag(1, q);
+        bias_vec(1, bv);
+
+        // ---- iteration t (t + 1 < ntiles), i = t mod 4 (see k_assign)
+        auto iteration = [&](int t, int i) {
+            floatx4(&cur)[RB][NP] = acc[(i & 1) ^ 1];
+            const floatx4(&prv)[RB][NP] = acc[i & 1];
+            const int b1 = (i + 1) % kAssignRing;  // tile t+1
+            const int b2 = (i + 2) % kAssignRing;  // tile t+2
+            const int b3 = (i + 3) % kAssignRing;  // receives tile t+3
+            gload(t + 4, st[i & 1]);
+            u32x4 nx[P];
+            floatx4 nbv[RB];
+            __builtin_amdgcn_sched_barrier(0);
+            epi_begin();
+#pragma unroll
+            for (int sl = 0; sl < kSlots; ++sl) {
+                const int s = sl / RB, rb = sl % RB;
+#pragma unroll
+                for (int r = 8 * sl / kSlots; r < 8 * (sl + 1) / kSlots; ++r) epi_row(prv, r);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int np = 0; np < NP; ++np)
+                    cur[rb][np] = M::step(a[sl], xf[np][s], s == 0 ? bv[rb] : cur[rb][np]);
+                // a[sl] is free: read the fragment needed P slots later
+                const int v = sl + P;
+                if (v < kSlots)
+                    a[v] = frag(b1, v);
+                else
+                    nx[v - kSlots] = frag(b2, v - kSlots);
+                if (sl == kBiasSlot) bias_vec(b2, nbv);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            epi_end(t);
+#pragma unroll
+            for (int q = 0; q < P; ++q) a[q] = nx[q];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) bv[rb] = nbv[rb];
+            sstore(b3, st[(i & 1) ^ 1]);
+            __syncthreads();
+        };
+        auto final_epilogue = [&](int t, const floatx4(&sc)[RB][NP]) {
+            epi_begin();
+#pragma unroll
+            for (int r = 0; r < 8; ++r) epi_row(sc, r);
+            epi_end(t);
+        };
+        int t = 0;
+        for (; t + 4 < ntiles; t += 4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) iteration(t + i, i);
+        }
+        switch (ntiles - t) {
+            case 1:
+                final_epilogue(t, acc[0]);
+                break;
+            case 2:
+                iteration(t, 0);
+                final_epilogue(t + 1, acc[1]);
+                break;
+            case 3:
+                iteration(t, 0);
+                iteration(t + 1, 1);
+                final_epilogue(t + 2, acc[0]);
+                break;
+            default:
+                iteration(t, 0);
+                iteration(t + 1, 1);
+                iteration(t + 2, 2);
+                final_epilogue(t + 3, acc[1]);
+                break;
+        }
+
+        // ---- merge the four row groups that hold the same point
+        // (lexicographic on (score, index)); write labels
+#pragma unroll
+        for (int np = 0; np < NP; ++np) {
+            float sc = best[np];
+            int32_t ix = bidx[np] + 4 * g;
+#pragma unroll
+            for (int o = 16; o <= 32; o <<= 1) {
+                const float so = __shfl_xor(sc, o);
+                const int32_t io = __shfl_xor(ix, o);
+                if (so > sc || (so == sc && io < ix)) {
+                    sc = so;
+                    ix = io;
+                }
+            }
+            // |x|^2 for min_dist, from the fragments still in registers
+            float xx = 0.f;
+            if (min_dist) {
+#pragma unroll
+                for (int s = 0; s < S; ++s) xx += MS::sumsq(xf[np][s]);
+                xx += __shfl_xor(xx, 16);
+                xx += __shfl_xor(xx, 32);
+            }
+            const int64_t j = pbase + np * 16 + col;
+            if (g == 0 && j < N) {
+                labels[b * N + j] = ix;
+                if (min_dist) min_dist[b * N + j] = xx - 2.f * sc;
+            }
+        }
+        __syncthreads();  // the next item's prologue rewrites the ring
+    }
+}
+
+template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK>
+hipError_t launch_assign16_t(const void* X, const void* C, const float* bias, int32_t* labels,
+                             float* min_dist, int64_t B, int64_t N, int64_t K, int d,
+                             hipStream_t s) {
+    constexpr int lds = kAssignRing * (kAssignBK * (4 * S * 16 + 16) + kAssignBK * 4);
+    static_assert(lds <= kLdsBytes, "LDS budget");
+    constexpr int PTS = kAssignWaves * NP * 16;
+    auto kern = k_assign16<T, S, NP, VEC, EXACT, SMALLK>;
+    static bool attr_set = false;  // one attribute call per instantiation and process
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int64_t grid = B * ((N + PTS - 1) / PTS);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kAssignWaves * kWave), lds, s,
+                       static_cast<const T*>(X), static_cast<const T*>(C), bias, labels, min_dist,
+                       B, N, K, d);
+    return hipGetLastError();
+}
+
+// 16-bit inputs with d <= 256: S = k-steps of 32 (a power of two covering
+// d), four 16-point blocks per wave (two for S = 8).
+template <typename T>
+hipError_t dispatch_assign16(const void* X, const void* C, const float* bias, int32_t* labels,
+                             float* min_dist, int64_t B, int64_t N, int64_t K, int d,
+                             hipStream_t s) {
+    const int need = (d + 31) / 32;
+    const bool vec = (d % 8) == 0;
+#define FK_ASSIGN16_CASE(SS, NPP)                                                              \
+    if (need <= SS) {                                                                          \
+        if (K < kAssignBK)                                                                     \
+            return vec ? launch_assign16_t<T, SS, NPP, true, false, true>(                     \
+                             X, C, bias, labels, min_dist, B, N, K, d, s)                      \
+                       : launch_assign16_t<T, SS, NPP, false, false, true>(                    \
+                             X, C, bias, labels, min_dist, B, N, K, d, s);                     \
+        if (vec && d == 32 * SS)                                                               \
+            return launch_assign16_t<T, SS, NPP, true, true, false>(X, C, bias, labels,        \
+                                                                    min_dist, B, N, K, d, s);  \
+        if (vec)                                                                               \
+            return launch_assign16_t<T, SS, NPP, true, false, false>(X, C, bias, labels,       \
+                                                                     min_dist, B, N, K, d, s); \
+        return launch_assign16_t<T, SS, NPP, false, false, false>(X, C, bias, labels, min_dist, \
+                                                                  B, N, K, d, s);              \
+    }
+    FK_ASSIGN16_CASE(1, 4)
+    FK_ASSIGN16_CASE(2, 4)
+    FK_ASSIGN16_CASE(4, 4)
+    FK_ASSIGN16_CASE(8, 2)
+#undef FK_ASSIGN16_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+}  // namespace fk

@@ -1,13 +1,15 @@
 // k_assign_bf16.hip -- instantiations of the fused assign kernels for __bf16 inputs.
+#include "k_assign16.inl"
 #include "k_assign_splitd.inl"
 
 namespace fk {
 // Rows up to 256 dimensions keep each wave's points in registers for the
-// whole K loop; longer rows stream d in chunks (split-d kernel).
+// whole K loop (16x16x32 matrix instructions); longer rows stream d in
+// chunks (split-d kernel).
 hipError_t launch_assign_bf16(const void* X, const void* C, const float* bias, int32_t* labels,
                          float* min_dist, int64_t B, int64_t N, int64_t K, int d, hipStream_t s) {
     if (d > 256)
         return launch_assign_splitd<__bf16>(X, C, bias, labels, min_dist, B, N, K, d, s);
-    return dispatch_assign<__bf16>(X, C, bias, labels, min_dist, B, N, K, d, s);
+    return dispatch_assign16<__bf16>(X, C, bias, labels, min_dist, B, N, K, d, s);
 }
 }  // namespace fk
