@@ -38,7 +38,8 @@ def log(*a):
 
 def assign_sources_hash() -> str:
     h = hashlib.sha256()
-    for f in ("k_assign.inl", "k_assign_f16.hip", "k_assign_bf16.hip", "k_assign_f32.hip"):
+    for f in ("k_assign.inl", "k_assign16.inl", "k_assign_splitd.inl", "k_assign_f16.hip",
+              "k_assign_bf16.hip", "k_assign_f32.hip"):
         with open(os.path.join(ROOT, "exact_lloyd_means_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -62,7 +63,12 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=25)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, help="workload 1..4 (see synth.CONFIGS)")
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload 1..5 (see synth.CONFIGS); 5 streams X from pinned host memory")
+    ap.add_argument("--points", type=int, default=0,
+                    help="workload 5 only: N (default: the workload's 2^27)")
+    ap.add_argument("--chunk", type=int, default=1 << 24,
+                    help="workload 5 only: points per streamed chunk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -90,6 +96,8 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = synth.CONFIGS[args.config]
+    if args.config == 5:
+        return run_streamed(args, w)
     fmt = w.dtype
     log(f"[bench] generating {synth.describe(w)}")
     t = time.time()
@@ -211,6 +219,132 @@ def main() -> int:
     return 0
 
 
+def run_streamed(args, w) -> int:
+    """Workload 5: X lives in pinned host memory and every iteration streams
+    it to the GPU in chunks (fk_lloyd_streamed, copies on their own stream
+    overlapped with compute).  One step = one Lloyd iteration."""
+    import numpy as np
+    import torch
+
+    import exact_lloyd_means_amd as fk
+    import synth
+
+    N = args.points or w.N
+    chunk = min(args.chunk, N)
+    log(f"[bench] generating {N} points into pinned host memory")
+    t = time.time()
+    X_host, C0 = synth.make_streamed(w, N=N, log=log)
+    log(f"[bench] generated in {time.time() - t:.1f}s")
+    B, _, d = X_host.shape
+    K = C0.shape[1]
+    fmt = w.dtype
+    C = C0.cuda()
+    labels = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    counts = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    ws = fk.workspace(fk.problem(B, N, K, d, X_host.dtype), "cuda", chunk)
+    copy = torch.cuda.Stream()
+
+    # K steps = one call running K iterations, so the copy of each
+    # iteration's first chunks overlaps the previous iteration's compute
+    def steps(k):
+        fk.fk_lloyd_streamed(X_host, C, labels, counts, k, chunk, ws=ws, copy_stream=copy)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    if args.warmup:
+        steps(args.warmup)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    steps(args.steps)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = e0.elapsed_time(e1)
+
+    # the two bounds of a streamed iteration, measured on one chunk: the
+    # pinned host-to-device copy and the fp32 assign on a resident chunk
+    xb = X_host[:, :chunk]
+    dev = torch.empty(xb.shape, dtype=xb.dtype, device="cuda")
+    for _ in range(2):
+        dev.copy_(xb, non_blocking=True)
+    torch.cuda.synchronize()
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record()
+    dev.copy_(xb, non_blocking=True)
+    c1.record()
+    torch.cuda.synchronize()
+    h2d_gbs = xb.numel() * xb.element_size() / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    bias = torch.empty((B, K), dtype=torch.float32, device="cuda")
+    fk.fk_centroid_bias(C, bias)
+    lab = torch.empty((B, chunk), dtype=torch.int32, device="cuda")
+    fk.fk_assign_with_bias(dev, C, bias, lab)
+    torch.cuda.synchronize()
+    a_ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    a_ev[0].record()
+    for _ in range(3):
+        fk.fk_assign_with_bias(dev, C, bias, lab)
+    a_ev[1].record()
+    torch.cuda.synchronize()
+    a_ms = a_ev[0].elapsed_time(a_ev[1]) / 3
+    a_flops = 2.0 * B * chunk * K * d
+    achieved_tf = a_flops / (a_ms * 1e-3) / 1e12
+    peak_tf = PEAK_TFLOPS[fmt]
+    nchunks = (N + chunk - 1) // chunk
+    bound_s = max(N * d * xb.element_size() / (h2d_gbs * 1e9), nchunks * a_ms * 1e-3)
+    value = args.steps / (total_ms * 1e-3)
+    src_hash = assign_sources_hash()
+    del dev
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = run_cpu_baseline(w, X_host, C.to(X_host.dtype), fmt, args.cpu_seconds, value)
+
+    out = {
+        "metric": f"Lloyd iters/sec at {synth.describe(w)}" + ("" if N == w.N else f" (N={N})"),
+        "value": round(value, 4),
+        "unit": "Lloyd it/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": fmt,
+        "data": f"synthetic: seeded Gaussian mixture generated into pinned host memory, "
+                f"streamed in chunks of {chunk} points",
+        "config": {"workload": w.name, "B": B, "N": N, "K": K, "d": d, "dtype": fmt,
+                   "chunk_points": chunk,
+                   "step": "1 Lloyd iteration streamed from host (fk_lloyd_streamed)"},
+        "stages": {
+            "h2d_GBps_one_chunk": round(h2d_gbs, 1),
+            "assign_ms_one_chunk": round(a_ms, 3),
+            "bound_ms_per_step": round(bound_s * 1e3, 2),
+            "fraction_of_bound": round(bound_s * 1e3 / (total_ms / args.steps), 4),
+            "wall_ms_per_step": round(wall * 1e3 / args.steps, 2),
+        },
+        "roofline": {
+            "kernel": "k_assign (fp32, one resident chunk in the streamed launch shape)",
+            "bound": "mfma",
+            "achieved": round(achieved_tf, 2),
+            "peak": peak_tf,
+            "unit": "TFLOP/s",
+            "frac": round(achieved_tf / peak_tf, 4),
+            "traffic": measured_traffic(w.name, src_hash),
+            "algorithmic_flops_per_launch": a_flops,
+            "assign_sources_sha256_16": src_hash,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def run_cpu_baseline(w, X_cpu, Cq, fmt, target_s, gpu_value):
     import numpy as np
     import torch
@@ -239,12 +373,14 @@ def run_cpu_baseline(w, X_cpu, Cq, fmt, target_s, gpu_value):
     t = time.perf_counter()
     lab, _, _ = oracle.assign(Xs, Cs, fmt_x=fmt, fmt_c=fmt, rows=rows)
     t_assign = (time.perf_counter() - t) * total / S
-    # update of one whole problem, scaled by B
-    lab0 = np.zeros((1, N), np.int32)
-    lab0[0, :] = np.arange(N) % Cs.shape[1]
+    # update of one problem (at most its first 2^22 points), scaled linearly
+    Nu = min(N, 1 << 22)
+    lab0 = np.zeros((1, Nu), np.int32)
+    lab0[0, :] = np.arange(Nu) % Cs.shape[1]
     t = time.perf_counter()
-    oracle.update(Xs[:1], lab0, np.zeros((1, Cs.shape[1], d), np.float32), fmt_x=fmt, fmt_c="f32")
-    t_update = (time.perf_counter() - t) * B
+    oracle.update(np.ascontiguousarray(Xs[:1, :Nu]), lab0, np.zeros((1, Cs.shape[1], d), np.float32),
+                  fmt_x=fmt, fmt_c="f32")
+    t_update = (time.perf_counter() - t) * B * N / Nu
     it_s = 1.0 / (t_assign + t_update)
     return {
         "value": it_s,
@@ -252,7 +388,8 @@ def run_cpu_baseline(w, X_cpu, Cq, fmt, target_s, gpu_value):
         "cores": threads,
         "kind": "oracle",
         "sample": (f"fp64 oracle assign on {S} random points of {total} (x{total / S:.1f} "
-                   f"extrapolated, linear in points) + update of 1 of {B} problems (x{B}); "
+                   f"extrapolated, linear in points) + update of {Nu} points of 1 of {B} problems "
+                   f"(x{B * N / Nu:g}); "
                    f"{t_assign:.1f} s assign + {t_update:.2f} s update per iteration"),
         "gpu_over_cpu": round(gpu_value / it_s, 1),
     }

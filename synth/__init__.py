@@ -23,7 +23,7 @@ import math
 import numpy as np
 import torch
 
-__all__ = ["Workload", "CONFIGS", "make", "integer_problem", "init_indices"]
+__all__ = ["Workload", "CONFIGS", "make", "make_streamed", "integer_problem", "init_indices"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -112,6 +112,37 @@ def make(cfg: int | Workload, N: int | None = None, B: int | None = None,
     X = X.to(_TORCH_DTYPE[dtype])
     idx = init_indices(w, B, N, K, seed=w.init_seed if seed == w.seed else seed + 1000)
     C0 = torch.gather(X, 1, idx.unsqueeze(-1).expand(B, K, d)).to(torch.float32)
+    return X, C0
+
+
+def make_streamed(cfg: int | Workload, N: int | None = None, piece: int = 1 << 22,
+                  log=None, pin: bool = True):
+    """Seeded (X_host, C0) for a single-problem workload too large to build
+    at once: X_host (1, N, d) is allocated in host memory (pinned unless
+    pin=False) and filled
+    piece by piece (piece j draws its component ids and noise from a
+    generator seeded with seed * 1000003 + j), so peak extra memory is one
+    piece.  Same distribution as make(); a different random stream.
+    C0 = the init points (fp32)."""
+    w = CONFIGS[cfg] if isinstance(cfg, int) else cfg
+    N = w.N if N is None else N
+    K, d = w.K, w.d
+    assert w.B == 1 and w.weights == "uniform" and not w.unit
+    g = torch.Generator().manual_seed(w.seed)
+    means = torch.randn((K, d), generator=g, dtype=torch.float32) * w.mean_std
+    X = torch.empty((1, N, d), dtype=_TORCH_DTYPE[w.dtype], pin_memory=pin)
+    for j, i0 in enumerate(range(0, N, piece)):
+        n = min(piece, N - i0)
+        gj = torch.Generator().manual_seed(w.seed * 1000003 + j)
+        z = torch.randint(0, K, (n,), generator=gj, dtype=torch.int64)
+        x = torch.randn((n, d), generator=gj, dtype=torch.float32)
+        x.mul_(w.sigma).add_(means[z])
+        X[0, i0:i0 + n].copy_(x)
+        if log and j % 8 == 0:
+            log(f"[synth] {i0 + n} of {N} points")
+    gi = torch.Generator().manual_seed(w.init_seed)
+    idx = torch.randperm(N, generator=gi)[:K]
+    C0 = X[0, idx].to(torch.float32).unsqueeze(0).contiguous()
     return X, C0
 
 
