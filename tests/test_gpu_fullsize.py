@@ -54,3 +54,27 @@ def test_full_size_lockstep(cfg):
         print(f"[fullsize] {w.name} iteration {it}: {st} {su}", flush=True)
         if w.dtype == "f32":
             Cq = C.clone()
+
+
+def test_streamed_full_chunk_lockstep():
+    """The pinned-host workload in the benchmark's streamed launch shape
+    (chunks of 2^24 points, copy stream overlapped with compute), at N = 2^25:
+    one iteration checked against the oracle (labels on a sample, counts and
+    centroids of the update on every point)."""
+    w = synth.CONFIGS[5]
+    N, chunk = 1 << 25, 1 << 24
+    print(f"[fullsize] {w.name} N={N}: generating", flush=True)
+    X_host, C0 = synth.make_streamed(w, N=N)
+    C = C0.cuda()
+    C_prev = C.clone()
+    labels = torch.empty((1, N), dtype=torch.int32, device="cuda")
+    counts = torch.empty((1, w.K), dtype=torch.int32, device="cuda")
+    copy = torch.cuda.Stream()
+    fk.fk_lloyd_streamed(X_host, C, labels, counts, 1, chunk, copy_stream=copy)
+    torch.cuda.synchronize()
+    rows = np.random.Generator(np.random.PCG64(505)).choice(N, size=2048, replace=False)
+    print(f"[fullsize] {w.name}: checking", flush=True)
+    st = check_labels(labels, X_host, C_prev, rows=rows)
+    su = check_update(X_host, labels, C_prev, C, counts)
+    assert int(counts.sum()) == N
+    print(f"[fullsize] {w.name}: {st} {su}", flush=True)
