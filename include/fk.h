@@ -134,7 +134,8 @@ fk_status fk_assign_with_bias(const fk_problem* p, const void* X, const void* C,
  * 关键设计 2: the 1-D label vector is argsorted so equal labels form
  * contiguous segments).  From labels [B][N] writes
  *   counts     [B][K]   number of points per label (exact);
- *   offsets    [B][K+1] exclusive prefix sums of counts (offsets[b][K] = N);
+ *   offsets    [B][K+1] exclusive prefix sums of counts (offsets[b][K] = the
+ *                       number of labels in [0, K), N when all are valid);
  *   sorted_idx [B][N]   point indices grouped by label: positions
  *                       offsets[b][k] .. offsets[b][k+1]-1 hold the points of
  *                       label k, in unspecified order within the segment.
@@ -147,16 +148,19 @@ fk_status fk_sort_labels(const fk_problem* p, const int32_t* labels, int32_t* co
 /*
  * fk_update -- new centroids from labels (papernotes.org notes, 关键设计 2):
  * argsort the labels, gather the rows of X of each contiguous same-label
- * segment (X is not moved), sum them in fp32 with one atomic add per segment
- * piece, then divide by the count.
+ * segment (X is not moved), sum them in fp32 on chip, then divide by the
+ * count.  A segment of at most 256 points is summed by one wave without
+ * atomics; a longer one is cut into pieces of 256 sorted positions, each
+ * adding its partial sum with one row of fp32 atomic adds.
  *   X [B][N][d] problem dtype; labels [B][N];
  *   C_prev [B][K][d] fp32, kept for empty clusters (may alias C_next);
  *   C_next [B][K][d] fp32 = sum / count (IEEE fp32 division);
  *   C_next_lowp [B][K][d] problem dtype = C_next rounded to nearest even,
  *     may be NULL (must be NULL or distinct from C_next for fp32);
  *   counts [B][K] int32.
- * Centroid low bits depend on the order of fp32 atomic additions and can
- * differ between runs; counts never do.
+ * For segments longer than 256 points the centroid low bits depend on the
+ * order of the fp32 atomic additions and can differ between runs; counts
+ * never do.  Labels outside [0, K) are skipped and counted (fk_error_count).
  */
 fk_status fk_update(const fk_problem* p, const void* X, const int32_t* labels,
                     const float* C_prev, float* C_next, void* C_next_lowp, int32_t* counts,
@@ -202,9 +206,10 @@ fk_status fk_lloyd_streamed(const fk_problem* p, const void* X_host, int64_t chu
                             size_t ws_bytes, void* compute_stream, void* copy_stream);
 
 /*
- * fk_error_count -- number of out-of-range labels skipped by the most recent
- * fk_sort_labels / fk_update / fk_lloyd that used workspace ws.  Synchronises
- * the stream.  *count is a host pointer.
+ * fk_error_count -- number of out-of-range labels (summed over the B
+ * problems) skipped by the most recent fk_sort_labels / fk_update /
+ * fk_lloyd that used workspace ws.  Synchronises the stream.  *count is a
+ * host pointer.
  */
 fk_status fk_error_count(const fk_problem* p, const void* ws, size_t ws_bytes, int64_t* count,
                          void* stream);
