@@ -45,6 +45,14 @@ def assign_sources_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def assign_kernel_name(fmt: str, d: int) -> str:
+    """The fused distance + argmin kernel that the library launches for this
+    element type and dimension."""
+    if fmt == "f32":
+        return "k_assign (fp32 32x32x2 MFMA)" if d <= 128 else "k_assign_splitd (fp32)"
+    return "k_assign16 (16x16x32 MFMA)" if d <= 256 else "k_assign_splitd (16-bit)"
+
+
 def measured_traffic(workload: str, src_hash: str):
     """HBM bytes per assign launch from the committed PMC summary, if it was
     taken on the current assign kernel sources."""
@@ -72,6 +80,13 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--groups", type=int, default=1,
+                    help="split the B problems into this many groups, each on its own stream, "
+                         "so one group's update can overlap another's assign")
+    ap.add_argument("--schedule", choices=("chain", "lockstep"), default="chain",
+                    help="chain: the groups' assigns run one after another (each waits for the "
+                         "previous one), so an update overlaps the next group's assign; "
+                         "lockstep: the groups run side by side with no cross-stream waits")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB -> 1 GiB copy kernel (PMC byte-counter calibration)")
     ap.add_argument("--summarize", nargs="+", metavar="ARG",
@@ -111,40 +126,73 @@ def main() -> int:
     bias = torch.empty((B, K), dtype=torch.float32, device="cuda")
     labels = torch.empty((B, N), dtype=torch.int32, device="cuda")
     counts = torch.empty((B, K), dtype=torch.int32, device="cuda")
-    ws = fk.workspace(fk.problem(B, N, K, d, X.dtype))
-    lowp = Cq if fmt != "f32" else None
+    # The B problems are independent: G groups of B/G problems run on G
+    # streams, so one group's (memory-bound) update overlaps another group's
+    # (matrix-bound) assign.  Each group's calls use their own workspace.
+    G = max(1, args.groups)
+    if B % G:
+        log(f"--groups {G} must divide B={B}")
+        return 2
+    Hg = B // G
+    grp = [slice(g * Hg, (g + 1) * Hg) for g in range(G)]
+    ws = [fk.workspace(fk.problem(Hg, N, K, d, X.dtype)) for _ in range(G)]
+    streams = [torch.cuda.Stream() for _ in range(G)]
+    chain = [torch.cuda.Event() for _ in range(G)]
+    last = [None]
 
-    def step(e=None):
-        if e:
-            e[0].record()
-        fk.fk_centroid_bias(Cq, bias)
-        if e:
-            e[1].record()
-        fk.fk_assign_with_bias(X, Cq, bias, labels)
-        if e:
-            e[2].record()
-        # in place: C_prev and C_next alias; the RNE copy feeds the next assign
-        fk.fk_update(X, labels, C, C, lowp, counts, ws=ws)
-        if e:
-            e[3].record()
+    def step(g, e=None):
+        sl = grp[g]
+        with torch.cuda.stream(streams[g]):
+            if e:
+                e[0].record()
+            fk.fk_centroid_bias(Cq[sl], bias[sl])
+            if e:
+                e[1].record()
+            if G > 1 and args.schedule == "chain" and last[0] is not None:
+                streams[g].wait_event(last[0])
+            if e:
+                e[4].record()
+            fk.fk_assign_with_bias(X[sl], Cq[sl], bias[sl], labels[sl])
+            if e:
+                e[2].record()
+            chain[g].record()
+            last[0] = chain[g]
+            # in place: C_prev and C_next alias; the RNE copy feeds the next assign
+            fk.fk_update(X[sl], labels[sl], C[sl], C[sl], Cq[sl] if fmt != "f32" else None,
+                         counts[sl], ws=ws[g])
+            if e:
+                e[3].record()
 
-    log(f"[bench] warmup {args.warmup} steps")
+    log(f"[bench] {G} stream group(s) of {Hg} problems ({args.schedule}); "
+        f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
-        step()
+        for g in range(G):
+            step(g)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(G)]
+           for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s])
+    main_stream = torch.cuda.current_stream()
+    start.record(main_stream)
+    for st in streams:
+        st.wait_event(start)
+    for s_ in range(args.steps):
+        for g in range(G):
+            step(g, evs[s_][g])
+    for st in streams:
+        main_stream.wait_stream(st)
+    end.record(main_stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = evs[0][0].elapsed_time(evs[-1][3])
-    bias_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    assign_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    update_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    total_ms = start.elapsed_time(end)
+    bias_ms = [e[0].elapsed_time(e[1]) for row in evs for e in row]
+    assign_ms = [e[4].elapsed_time(e[2]) for row in evs for e in row]
+    update_ms = [e[2].elapsed_time(e[3]) for row in evs for e in row]
     log(f"[bench] {args.steps} steps: {total_ms:.3f} ms (events), {wall * 1e3:.3f} ms (wall)")
 
     if args.copy_calibration:
@@ -157,10 +205,10 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    flops = 2.0 * B * N * K * d
+    flops = 2.0 * Hg * N * K * d  # per assign launch (one group)
     xb = 4 if fmt == "f32" else 2
-    upd_bytes = B * N * d * xb + B * N * 4 + B * K * d * 4 + (B * K * d * xb if fmt != "f32" else 0) \
-        + B * K * 4
+    upd_bytes = Hg * N * d * xb + Hg * N * 4 + Hg * K * d * 4 \
+        + (Hg * K * d * xb if fmt != "f32" else 0) + Hg * K * 4  # per update call
     a_mean = float(np.mean(assign_ms))
     u_mean = float(np.mean(update_ms))
     achieved_tf = flops / (a_mean * 1e-3) / 1e12
@@ -201,7 +249,7 @@ def main() -> int:
             "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         },
         "roofline": {
-            "kernel": "k_assign (fused distance + argmin)",
+            "kernel": assign_kernel_name(fmt, d),
             "bound": "mfma",
             "achieved": round(achieved_tf, 2),
             "peak": peak_tf,
@@ -444,7 +492,10 @@ def summarize(argv) -> int:
                             "assign_dispatches": len(assign),
                             "copy_1GiB_counted_kib": kib_copy, "calibration_factor": factor}
         hbm = sum(r["assign_kib_per_dispatch"] * 1024 * r["calibration_factor"] for r in res.values())
-        rec = {"workload": workload, "kernel": "k_assign", "command": cmd,
+        names = sorted({_short_name(k) for k in
+                        (r["Kernel_Name"] for r in csv.DictReader(open(fetch_csv)))
+                        if "k_assign" in k})
+        rec = {"workload": workload, "kernel": ", ".join(names), "command": cmd,
                "counters": res, "hbm_bytes_per_launch": round(hbm),
                "assign_sources_sha256_16": assign_sources_hash()}
         print(json.dumps(rec, indent=1))
