@@ -87,6 +87,9 @@ def main() -> int:
                     help="chain: the groups' assigns run one after another (each waits for the "
                          "previous one), so an update overlaps the next group's assign; "
                          "lockstep: the groups run side by side with no cross-stream waits")
+    ap.add_argument("--no-baselines", action="store_true",
+                    help="skip timing the unfused baselines (materialised scores + argmin, "
+                         "scatter-atomic update)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB -> 1 GiB copy kernel (PMC byte-counter calibration)")
     ap.add_argument("--summarize", nargs="+", metavar="ARG",
@@ -136,7 +139,7 @@ def main() -> int:
     Hg = B // G
     grp = [slice(g * Hg, (g + 1) * Hg) for g in range(G)]
     ws = [fk.workspace(fk.problem(Hg, N, K, d, X.dtype)) for _ in range(G)]
-    streams = [torch.cuda.Stream() for _ in range(G)]
+    streams = [torch.cuda.Stream() for _ in range(G)] if G > 1 else [torch.cuda.current_stream()]
     chain = [torch.cuda.Event() for _ in range(G)]
     last = [None]
 
@@ -217,6 +220,10 @@ def main() -> int:
     value = args.steps / (total_ms * 1e-3)
     src_hash = assign_sources_hash()
 
+    base = None
+    if not args.no_baselines:
+        base = run_baselines(X, Cq, C, labels, fmt, a_mean * G, u_mean * G)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = run_cpu_baseline(w, X_cpu, Cq, fmt, args.cpu_seconds, value)
@@ -260,11 +267,69 @@ def main() -> int:
             "assign_sources_sha256_16": src_hash,
         },
         "cpu_baseline": cpu,
+        "unfused_baselines": base,
     }
     if pages_ms:
         out["baseline_context"] = f"pages: {pages_ms} ms/iter on NVIDIA H200 (FP16), not this machine"
     print(json.dumps(out), flush=True)
     return 0
+
+
+def run_baselines(X, Cq, C, labels, fmt, fused_assign_ms, fused_update_ms, reps=3):
+    """Times the unfused forms of the two stages on the same inputs and
+    hardware: the assignment through a materialised B x N x K fp32 score
+    matrix (scores, then argmin) and the scatter-atomic update, against the
+    fused assign and the sort-inverse update of the timed steps (per step,
+    all problems)."""
+    import torch
+
+    import exact_lloyd_means_amd as fk
+
+    B, N, d = X.shape
+    K = Cq.shape[1]
+    out = {"fused_assign_ms": round(fused_assign_ms, 4),
+           "sort_inverse_update_ms": round(fused_update_ms, 4)}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        for _ in range(reps):
+            fn()
+        e[1].record()
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) / reps
+
+    bias = torch.empty((B, K), dtype=torch.float32, device="cuda")
+    fk.fk_centroid_bias(Cq, bias)
+    if fmt != "f32" and d <= 256:
+        log(f"[bench] unfused assign: {B * N * K * 4 / 2**30:.1f} GiB score matrix")
+        D = torch.empty((B, N, K), dtype=torch.float32, device="cuda")
+        lab = torch.empty_like(labels)
+        s_ms = timed(lambda: fk.fk_baseline_scores(X, Cq, bias, D))
+        m_ms = timed(lambda: fk.fk_baseline_argmin(D, lab))
+        fused = torch.empty_like(labels)
+        fk.fk_assign_with_bias(X, Cq, bias, fused)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(lab, fused))
+        del D
+        tot = s_ms + m_ms
+        out["materialised_assign"] = {
+            "scores_ms": round(s_ms, 4), "argmin_ms": round(m_ms, 4), "total_ms": round(tot, 4),
+            "score_matrix_bytes": B * N * K * 4,
+            "argmin_read_GBps": round(B * N * K * 4 / (m_ms * 1e-3) / 1e9, 1),
+            "labels_identical_to_fused": same}
+        out["assign_speedup"] = round(tot / fused_assign_ms, 2)
+    log("[bench] unfused update: scatter atomics")
+    sums = torch.empty((B, K, d), dtype=torch.float32, device="cuda")
+    Cn = torch.empty_like(C)
+    low = torch.empty_like(Cq) if fmt != "f32" else None
+    cnt = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    u_ms = timed(lambda: fk.fk_baseline_update_scatter(X, labels, C, Cn, low, cnt, sums))
+    out["scatter_update_ms"] = round(u_ms, 4)
+    out["update_speedup"] = round(u_ms / fused_update_ms, 2)
+    return out
 
 
 def run_streamed(args, w) -> int:

@@ -53,6 +53,10 @@ _SIG = {
                            _P, _P], ctypes.c_int),
     "fk_error_count": ([_PP, _P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int64), _P],
                        ctypes.c_int),
+    # include/fk_baseline.h
+    "fk_baseline_scores": ([_PP, _P, _P, _P, _P, _P], ctypes.c_int),
+    "fk_baseline_argmin": ([_PP, _P, _P, _P], ctypes.c_int),
+    "fk_baseline_update_scatter": ([_PP, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIG.items():
     _fn = getattr(lib, _name)
@@ -202,3 +206,32 @@ def fk_error_count(p: Problem, ws: torch.Tensor, stream=None) -> int:
     _check(lib.fk_error_count(ctypes.byref(p), _ptr(ws), ws.numel(), ctypes.byref(n),
                               _stream(stream)), "fk_error_count")
     return n.value
+
+
+# ---- baselines (include/fk_baseline.h): the unfused forms, for comparison --
+
+def fk_baseline_scores(X: torch.Tensor, C: torch.Tensor, bias: torch.Tensor,
+                       D: torch.Tensor, stream=None) -> None:
+    """D (B, N, K) fp32 = X . C^T + bias, written to memory in full."""
+    p = _problem_from(X, C.shape[1])
+    if C.dtype != X.dtype:
+        raise ValueError("C must have the dtype of X")
+    _check(lib.fk_baseline_scores(ctypes.byref(p), _ptr(X), _ptr(C), _ptr(bias), _ptr(D),
+                                  _stream(stream)), "fk_baseline_scores")
+
+
+def fk_baseline_argmin(D: torch.Tensor, labels: torch.Tensor, stream=None) -> None:
+    B, N, K = D.shape
+    p = problem(B, N, K, 1, torch.float32)
+    _check(lib.fk_baseline_argmin(ctypes.byref(p), _ptr(D), _ptr(labels), _stream(stream)),
+           "fk_baseline_argmin")
+
+
+def fk_baseline_update_scatter(X: torch.Tensor, labels: torch.Tensor, C_prev: torch.Tensor,
+                               C_next: torch.Tensor, C_next_lowp: torch.Tensor | None,
+                               counts: torch.Tensor, sums: torch.Tensor, stream=None) -> None:
+    p = _problem_from(X, C_prev.shape[1])
+    _check(lib.fk_baseline_update_scatter(ctypes.byref(p), _ptr(X), _ptr(labels), _ptr(C_prev),
+                                          _ptr(C_next), _ptr(C_next_lowp), _ptr(counts),
+                                          _ptr(sums), _stream(stream)),
+           "fk_baseline_update_scatter")

@@ -21,8 +21,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfk.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["fk_api.hip", "k_update.hip", "k_assign_f16.hip", "k_assign_bf16.hip",
-           "k_assign_f32.hip"]
+SOURCES = ["fk_api.hip", "k_update.hip", "k_baseline.hip", "k_assign_f16.hip",
+           "k_assign_bf16.hip", "k_assign_f32.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -25,6 +25,17 @@ hipError_t launch_assign(int dtype, const void* X, const void* C, const float* b
     }
 }
 
+hipError_t launch_scores_f16(const void*, const void*, const float*, float*, int64_t, int64_t,
+                             int64_t, int, hipStream_t);
+hipError_t launch_scores_bf16(const void*, const void*, const float*, float*, int64_t, int64_t,
+                              int64_t, int, hipStream_t);
+
+hipError_t launch_scores(int dtype, const void* X, const void* C, const float* bias, float* D,
+                         int64_t B, int64_t N, int64_t K, int d, hipStream_t s) {
+    return dtype == FK_F16 ? launch_scores_f16(X, C, bias, D, B, N, K, d, s)
+                           : launch_scores_bf16(X, C, bias, D, B, N, K, d, s);
+}
+
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 Workspace workspace_layout(const fk_problem& p, char* base) {
@@ -465,6 +476,61 @@ fk_status fk_error_count(const fk_problem* p, const void* ws, size_t ws_bytes, i
         for (int64_t i = 0; i < nb; ++i) total += part[i];
     }
     *count = total;
+    return FK_OK;
+}
+
+// ---- baselines ---------------------------------------------------------------
+
+fk_status fk_baseline_scores(const fk_problem* p, const void* X, const void* C, const float* bias,
+                             float* D, void* stream) {
+    FK_CHECK(check_problem(p));
+    FK_CHECK(check_ptr(X, "X"));
+    FK_CHECK(check_ptr(C, "C"));
+    FK_CHECK(check_ptr(bias, "bias"));
+    FK_CHECK(check_ptr(D, "D"));
+    if (p->dtype == FK_F32) return fail(FK_EUNSUPPORTED, "scores baseline takes fp16 or bf16");
+    if (p->d > 256) return fail(FK_EUNSUPPORTED, "scores baseline supports d <= 256");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    FK_TRY(launch_scores(p->dtype, X, C, bias, D, p->B, p->N, p->K, (int)p->d, s), "scores");
+    return FK_OK;
+}
+
+fk_status fk_baseline_argmin(const fk_problem* p, const float* D, int32_t* labels, void* stream) {
+    FK_CHECK(check_problem(p));
+    FK_CHECK(check_ptr(D, "D"));
+    FK_CHECK(check_ptr(labels, "labels"));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    FK_TRY(launch_argmin_rows(D, labels, p->B * p->N, p->K, s), "argmin");
+    return FK_OK;
+}
+
+fk_status fk_baseline_update_scatter(const fk_problem* p, const void* X, const int32_t* labels,
+                                     const float* C_prev, float* C_next, void* C_next_lowp,
+                                     int32_t* counts, float* sums, void* stream) {
+    FK_CHECK(check_problem(p));
+    FK_CHECK(check_ptr(X, "X"));
+    FK_CHECK(check_ptr(labels, "labels"));
+    FK_CHECK(check_ptr(C_prev, "C_prev"));
+    FK_CHECK(check_ptr(C_next, "C_next"));
+    FK_CHECK(check_ptr(C_next_lowp, "C_next_lowp", false));
+    FK_CHECK(check_ptr(counts, "counts"));
+    FK_CHECK(check_ptr(sums, "sums"));
+    if (p->dtype == FK_F32 && C_next_lowp && C_next_lowp == static_cast<void*>(C_next))
+        return fail(FK_EINVAL, "C_next_lowp must differ from C_next");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t rows = p->B * p->K;
+    FK_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(counts), rows, 0u, s), "clear counts");
+    FK_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(sums), rows * p->d, 0u, s), "clear sums");
+    FK_TRY(launch_scatter_add(p->dtype, X, labels, sums, counts, p->B, p->N, p->K, (int)p->d, s),
+           "scatter add");
+    FK_TRY(launch_finalize(p->dtype, sums, counts, C_prev, C_next,
+                           p->dtype == FK_F32 ? nullptr : C_next_lowp, nullptr, nullptr, rows,
+                           (int)p->d, s),
+           "finalize");
+    if (p->dtype == FK_F32 && C_next_lowp)
+        FK_TRY(hipMemcpyAsync(C_next_lowp, C_next, (size_t)(rows * p->d) * sizeof(float),
+                              hipMemcpyDeviceToDevice, s),
+               "copy fp32 centroids");
     return FK_OK;
 }
 

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "../../include/fk.h"
+#include "../../include/fk_baseline.h"
 
 namespace fk {
 
@@ -136,5 +137,19 @@ hipError_t launch_segment_sums(int dtype, const void* X, const int32_t* sorted_i
 hipError_t launch_finalize(int dtype, float* sums, const int32_t* counts, const float* C_prev,
                            float* C_next, void* lowp, float* bias, uint32_t* move_max,
                            int64_t rows, int d, hipStream_t s);
+
+// ---- baselines: materialised scores + argmin, scatter-atomic update --------
+// D [B][N][K] fp32 = x.c + bias for 16-bit inputs with d <= 256.
+hipError_t launch_scores(int dtype, const void* X, const void* C, const float* bias, float* D,
+                         int64_t B, int64_t N, int64_t K, int d, hipStream_t s);
+
+// labels[r] = lowest index of the largest of D[r][0..K)
+hipError_t launch_argmin_rows(const float* D, int32_t* labels, int64_t rows, int64_t K,
+                              hipStream_t s);
+
+// sums[b][labels[b][i]] += X[b][i] and counts[b][labels[b][i]] += 1 with atomics
+hipError_t launch_scatter_add(int dtype, const void* X, const int32_t* labels, float* sums,
+                              int32_t* counts, int64_t B, int64_t N, int64_t K, int d,
+                              hipStream_t s);
 
 }  // namespace fk

@@ -42,7 +42,9 @@ struct Mfma16<__bf16> {
 };
 
 // S = k-steps of 32 dimensions (d <= 32 S), NP = 16-point column blocks held
-// by each wave, VEC / EXACT / SMALLK as in k_assign.
+// by each wave, VEC / EXACT / SMALLK as in k_assign.  MAT: instead of the
+// running argmax, every score is written to D [B][N][K] fp32 (the distance
+// matrix the fused kernel exists to avoid; a baseline for comparison).
 //
 // Tile of 32 centroids = 2 row blocks of 16.  A slot is the NP MFMAs that
 // share one centroid fragment (row block rb, k-step s), slot order s-major;
@@ -50,11 +52,12 @@ struct Mfma16<__bf16> {
 // NP point blocks.  Staging (registers -> ring of four LDS buffers), the
 // prefetch of the next tile's fragments and bias, and the branch-free
 // overlapping last tile are those of k_assign.
-template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK>
-__global__ __launch_bounds__(kAssignWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void k_assign16(const T* __restrict__ X, const T* __restrict__ C, const float* __restrict__ bias,
-                int32_t* __restrict__ labels, float* __restrict__ min_dist, int64_t B, int64_t N,
-                int64_t K, int d) {
+template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK, bool MAT>
+__device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* __restrict__ C,
+                                              const float* __restrict__ bias,
+                                              int32_t* __restrict__ labels,
+                                              float* __restrict__ min_dist, int64_t B, int64_t N,
+                                              int64_t K, int d, float* __restrict__ D) {
     using M = Mfma16<T>;
     using MS = Mfma<T>;
     constexpr int V = 8;                               // elements per 16-byte chunk
@@ -191,6 +194,28 @@ void k_assign16(const T* __restrict__ X, const T* __restrict__ C, const float* _
                 rt[np] = keep ? rt[np] : 16 * rb + i;
             }
         };
+        // MAT: lane (g, col) holds scores of centroids 16 rb + 4 g + i
+        // (i = 0..3) of point col of each block
+        auto mat_store = [&](int t, const floatx4(&sc)[RB][NP]) {
+            const int32_t kb = tile_base(t);
+#pragma unroll
+            for (int np = 0; np < NP; ++np) {
+                const int64_t j = pbase + np * 16 + col;
+                if (j >= N) continue;
+                float* row = D + (b * N + j) * K;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const int k0 = kb + 16 * rb + 4 * g;
+                    if (!SMALLK && (K32 & 3) == 0) {  // then kb, k0 and each row are 16-byte aligned
+                        *reinterpret_cast<floatx4*>(row + k0) = sc[rb][np];
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (k0 + i < K32) row[k0 + i] = sc[rb][np][i];
+                    }
+                }
+            }
+        };
         auto epi_end = [&](int t) {
             const int32_t kb = tile_base(t);
 #pragma unroll
@@ -239,12 +264,17 @@ void k_assign16(const T* __restrict__ X, const T* __restrict__ C, const float* _
             u32x4 nx[P];
             floatx4 nbv[RB];
             __builtin_amdgcn_sched_barrier(0);
-            epi_begin();
+            if constexpr (MAT)
+                mat_store(t, prv);
+            else
+                epi_begin();
 #pragma unroll
             for (int sl = 0; sl < kSlots; ++sl) {
                 const int s = sl / RB, rb = sl % RB;
+                if constexpr (!MAT) {
 #pragma unroll
-                for (int r = 8 * sl / kSlots; r < 8 * (sl + 1) / kSlots; ++r) epi_row(prv, r);
+                    for (int r = 8 * sl / kSlots; r < 8 * (sl + 1) / kSlots; ++r) epi_row(prv, r);
+                }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int np = 0; np < NP; ++np)
@@ -258,7 +288,7 @@ void k_assign16(const T* __restrict__ X, const T* __restrict__ C, const float* _
                 if (sl == kBiasSlot) bias_vec(b2, nbv);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            epi_end(t);
+            if constexpr (!MAT) epi_end(t);
 #pragma unroll
             for (int q = 0; q < P; ++q) a[q] = nx[q];
 #pragma unroll
@@ -267,6 +297,10 @@ void k_assign16(const T* __restrict__ X, const T* __restrict__ C, const float* _
             __syncthreads();
         };
         auto final_epilogue = [&](int t, const floatx4(&sc)[RB][NP]) {
+            if constexpr (MAT) {
+                mat_store(t, sc);
+                return;
+            }
             epi_begin();
 #pragma unroll
             for (int r = 0; r < 8; ++r) epi_row(sc, r);
@@ -301,7 +335,7 @@ void k_assign16(const T* __restrict__ X, const T* __restrict__ C, const float* _
         // ---- merge the four row groups that hold the same point
         // (lexicographic on (score, index)); write labels
 #pragma unroll
-        for (int np = 0; np < NP; ++np) {
+        for (int np = 0; np < (MAT ? 0 : NP); ++np) {
             float sc = best[np];
             int32_t ix = bidx[np] + 4 * g;
 #pragma unroll
@@ -332,24 +366,49 @@ void k_assign16(const T* __restrict__ X, const T* __restrict__ C, const float* _
 }
 
 template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK>
+__global__ __launch_bounds__(kAssignWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_assign16(const T* __restrict__ X, const T* __restrict__ C, const float* __restrict__ bias,
+                int32_t* __restrict__ labels, float* __restrict__ min_dist, int64_t B, int64_t N,
+                int64_t K, int d) {
+    assign16_body<T, S, NP, VEC, EXACT, SMALLK, false>(X, C, bias, labels, min_dist, B, N, K, d,
+                                                       nullptr);
+}
+
+// The same contraction writing every score (MAT) instead of the argmax.
+template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK>
+__global__ __launch_bounds__(kAssignWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_scores16(const T* __restrict__ X, const T* __restrict__ C, const float* __restrict__ bias,
+                float* __restrict__ D, int64_t B, int64_t N, int64_t K, int d) {
+    assign16_body<T, S, NP, VEC, EXACT, SMALLK, true>(X, C, bias, nullptr, nullptr, B, N, K, d, D);
+}
+
+template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK, bool MAT = false>
 hipError_t launch_assign16_t(const void* X, const void* C, const float* bias, int32_t* labels,
                              float* min_dist, int64_t B, int64_t N, int64_t K, int d,
-                             hipStream_t s) {
+                             hipStream_t s, float* D = nullptr) {
     constexpr int lds = kAssignRing * (kAssignBK * (4 * S * 16 + 16) + kAssignBK * 4);
     static_assert(lds <= kLdsBytes, "LDS budget");
     constexpr int PTS = kAssignWaves * NP * 16;
-    auto kern = k_assign16<T, S, NP, VEC, EXACT, SMALLK>;
+    const void* kern;
+    if constexpr (MAT)
+        kern = reinterpret_cast<const void*>(k_scores16<T, S, NP, VEC, EXACT, SMALLK>);
+    else
+        kern = reinterpret_cast<const void*>(k_assign16<T, S, NP, VEC, EXACT, SMALLK>);
     static bool attr_set = false;  // one attribute call per instantiation and process
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int64_t grid = B * ((N + PTS - 1) / PTS);
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kAssignWaves * kWave), lds, s,
-                       static_cast<const T*>(X), static_cast<const T*>(C), bias, labels, min_dist,
-                       B, N, K, d);
+    const dim3 grid((unsigned)(B * ((N + PTS - 1) / PTS)));
+    if constexpr (MAT)
+        hipLaunchKernelGGL((k_scores16<T, S, NP, VEC, EXACT, SMALLK>), grid,
+                           dim3(kAssignWaves * kWave), lds, s, static_cast<const T*>(X),
+                           static_cast<const T*>(C), bias, D, B, N, K, d);
+    else
+        hipLaunchKernelGGL((k_assign16<T, S, NP, VEC, EXACT, SMALLK>), grid,
+                           dim3(kAssignWaves * kWave), lds, s, static_cast<const T*>(X),
+                           static_cast<const T*>(C), bias, labels, min_dist, B, N, K, d);
     return hipGetLastError();
 }
 
@@ -382,6 +441,33 @@ hipError_t dispatch_assign16(const void* X, const void* C, const float* bias, in
     FK_ASSIGN16_CASE(4, 4)
     FK_ASSIGN16_CASE(8, 2)
 #undef FK_ASSIGN16_CASE
+    return hipErrorInvalidValue;
+}
+
+// All scores x.c + bias into D [B][N][K] fp32, d <= 256 (same contraction,
+// tiles and dispatch as dispatch_assign16).
+template <typename T>
+hipError_t dispatch_scores16(const void* X, const void* C, const float* bias, float* D, int64_t B,
+                             int64_t N, int64_t K, int d, hipStream_t s) {
+    const int need = (d + 31) / 32;
+    const bool vec = (d % 8) == 0;
+#define FK_SCORES16_CASE(SS, NPP)                                                                \
+    if (need <= SS) {                                                                            \
+        if (K < kAssignBK)                                                                       \
+            return vec ? launch_assign16_t<T, SS, NPP, true, false, true, true>(                 \
+                             X, C, bias, nullptr, nullptr, B, N, K, d, s, D)                     \
+                       : launch_assign16_t<T, SS, NPP, false, false, true, true>(                \
+                             X, C, bias, nullptr, nullptr, B, N, K, d, s, D);                    \
+        return vec ? launch_assign16_t<T, SS, NPP, true, false, false, true>(                    \
+                         X, C, bias, nullptr, nullptr, B, N, K, d, s, D)                         \
+                   : launch_assign16_t<T, SS, NPP, false, false, false, true>(                   \
+                         X, C, bias, nullptr, nullptr, B, N, K, d, s, D);                        \
+    }
+    FK_SCORES16_CASE(1, 4)
+    FK_SCORES16_CASE(2, 4)
+    FK_SCORES16_CASE(4, 4)
+    FK_SCORES16_CASE(8, 2)
+#undef FK_SCORES16_CASE
     return hipErrorInvalidValue;
 }
 

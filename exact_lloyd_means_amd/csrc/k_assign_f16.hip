@@ -12,4 +12,9 @@ hipError_t launch_assign_f16(const void* X, const void* C, const float* bias, in
         return launch_assign_splitd<_Float16>(X, C, bias, labels, min_dist, B, N, K, d, s);
     return dispatch_assign16<_Float16>(X, C, bias, labels, min_dist, B, N, K, d, s);
 }
+// Scores mode of the same kernel (d <= 256): every x.c + bias into D.
+hipError_t launch_scores_f16(const void* X, const void* C, const float* bias, float* D, int64_t B,
+                          int64_t N, int64_t K, int d, hipStream_t s) {
+    return dispatch_scores16<_Float16>(X, C, bias, D, B, N, K, d, s);
+}
 }  // namespace fk

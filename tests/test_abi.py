@@ -2,6 +2,7 @@
 header declares, and rejects bad arguments with the documented status before
 touching the device (fake device addresses are never dereferenced)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -9,24 +10,27 @@ import pytest
 
 import exact_lloyd_means_amd as fk
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                      "include", "fk.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADER = os.path.join(INCLUDE, "fk.h")
 
 FAKE = 0x10000          # 16-byte aligned, never dereferenced
 FAKE_MISALIGNED = 0x10004
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fk_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for path in sorted(glob.glob(os.path.join(INCLUDE, "*.h"))):
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"\b(fk_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_symbols_exported():
     names = declared_functions()
     assert "fk_assign" in names and "fk_update" in names and "fk_lloyd" in names
+    assert "fk_baseline_scores" in names and "fk_baseline_update_scatter" in names
     for name in names:
-        assert hasattr(fk.lib, name), f"{name} declared in fk.h but not exported"
+        assert hasattr(fk.lib, name), f"{name} declared in include/ but not exported"
 
 
 def test_abi_version_matches_header():
@@ -115,6 +119,30 @@ def test_update_and_lloyd_validation():
                               None) == fk.FK_EINVAL
     # error count: host pointer missing
     assert lib.fk_error_count(ctypes.byref(p), FAKE, n, None, None) == fk.FK_EINVAL
+
+
+def test_baseline_validation():
+    lib = fk.lib
+    p = P()
+    ok = dict(X=FAKE, C=FAKE, bias=FAKE, D=FAKE)
+    # scores: 16-bit and d <= 256 only, every pointer required and aligned
+    assert lib.fk_baseline_scores(ctypes.byref(P(dtype=fk.FK_F32)), *ok.values(),
+                                  None) == fk.FK_EUNSUPPORTED
+    assert lib.fk_baseline_scores(ctypes.byref(P(d=257)), *ok.values(), None) == fk.FK_EUNSUPPORTED
+    for name in ok:
+        args = dict(ok, **{name: None})
+        assert lib.fk_baseline_scores(ctypes.byref(p), *args.values(), None) == fk.FK_EINVAL
+        args = dict(ok, **{name: FAKE_MISALIGNED})
+        assert lib.fk_baseline_scores(ctypes.byref(p), *args.values(), None) == fk.FK_EINVAL
+    assert lib.fk_baseline_argmin(ctypes.byref(p), None, FAKE, None) == fk.FK_EINVAL
+    assert lib.fk_baseline_argmin(ctypes.byref(P(K=0)), FAKE, FAKE, None) == fk.FK_EINVAL
+    # scatter update: sums required; fp32 low copy must not alias C_next
+    assert lib.fk_baseline_update_scatter(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                          None, None) == fk.FK_EINVAL
+    q = P(dtype=fk.FK_F32)
+    assert lib.fk_baseline_update_scatter(ctypes.byref(q), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          FAKE, None) == fk.FK_EINVAL
+    assert b"differ" in lib.fk_last_error()
 
 
 def test_workspace_has_no_NK_term():
