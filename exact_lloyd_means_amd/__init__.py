@@ -26,13 +26,14 @@ lib = ctypes.CDLL(LIB_PATH)
 
 FK_F32, FK_F16, FK_BF16 = 0, 1, 2
 FK_OK, FK_EINVAL, FK_EUNSUPPORTED, FK_EWORKSPACE, FK_EHIP, FK_EHOST = 0, -1, -2, -3, -4, -5
+FK_DETERMINISTIC = 1
 
 DTYPES = {torch.float32: FK_F32, torch.float16: FK_F16, torch.bfloat16: FK_BF16}
 
 
 class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
-                ("d", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("d", ctypes.c_int64), ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -77,9 +78,9 @@ def _check(status: int, where: str) -> None:
         raise FKError(status, where)
 
 
-def problem(B: int, N: int, K: int, d: int, dtype) -> Problem:
+def problem(B: int, N: int, K: int, d: int, dtype, deterministic: bool = False) -> Problem:
     code = DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
-    return Problem(B, N, K, d, code, 0)
+    return Problem(B, N, K, d, code, FK_DETERMINISTIC if deterministic else 0)
 
 
 def _ptr(t: torch.Tensor | None):
@@ -98,11 +99,11 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(int(stream))
 
 
-def _problem_from(X: torch.Tensor, K: int) -> Problem:
+def _problem_from(X: torch.Tensor, K: int, deterministic: bool = False) -> Problem:
     if X.dim() != 3:
         raise ValueError("X must be (B, N, d)")
     B, N, d = X.shape
-    return problem(B, N, K, d, X.dtype)
+    return problem(B, N, K, d, X.dtype, deterministic)
 
 
 def abi_version() -> int:
@@ -152,9 +153,10 @@ def fk_assign_with_bias(X: torch.Tensor, C: torch.Tensor, bias: torch.Tensor,
 
 def fk_sort_labels(labels: torch.Tensor, K: int, counts: torch.Tensor, offsets: torch.Tensor,
                    sorted_idx: torch.Tensor, ws: torch.Tensor | None = None,
-                   stream=None, d: int = 1, dtype=torch.float32) -> None:
+                   stream=None, d: int = 1, dtype=torch.float32,
+                   deterministic: bool = False) -> None:
     B, N = labels.shape
-    p = problem(B, N, K, d, dtype)
+    p = problem(B, N, K, d, dtype, deterministic)
     ws = workspace(p, labels.device) if ws is None else ws
     _check(lib.fk_sort_labels(ctypes.byref(p), _ptr(labels), _ptr(counts), _ptr(offsets),
                               _ptr(sorted_idx), _ptr(ws), ws.numel(), _stream(stream)),
@@ -163,8 +165,8 @@ def fk_sort_labels(labels: torch.Tensor, K: int, counts: torch.Tensor, offsets: 
 
 def fk_update(X: torch.Tensor, labels: torch.Tensor, C_prev: torch.Tensor, C_next: torch.Tensor,
               C_next_lowp: torch.Tensor | None, counts: torch.Tensor,
-              ws: torch.Tensor | None = None, stream=None) -> None:
-    p = _problem_from(X, C_prev.shape[1])
+              ws: torch.Tensor | None = None, stream=None, deterministic: bool = False) -> None:
+    p = _problem_from(X, C_prev.shape[1], deterministic)
     ws = workspace(p, X.device) if ws is None else ws
     _check(lib.fk_update(ctypes.byref(p), _ptr(X), _ptr(labels), _ptr(C_prev), _ptr(C_next),
                          _ptr(C_next_lowp), _ptr(counts), _ptr(ws), ws.numel(),
@@ -173,10 +175,10 @@ def fk_update(X: torch.Tensor, labels: torch.Tensor, C_prev: torch.Tensor, C_nex
 
 def fk_lloyd(X: torch.Tensor, C: torch.Tensor, labels: torch.Tensor, counts: torch.Tensor,
              max_iters: int, tol: float = 0.0, want_n_iter: bool = False,
-             ws: torch.Tensor | None = None, stream=None):
+             ws: torch.Tensor | None = None, stream=None, deterministic: bool = False):
     """Runs Lloyd iterations in place on the fp32 centroids C.  Returns the
     number of iterations run when want_n_iter (one sync per iteration)."""
-    p = _problem_from(X, C.shape[1])
+    p = _problem_from(X, C.shape[1], deterministic)
     ws = workspace(p, X.device) if ws is None else ws
     n = ctypes.c_int(0)
     _check(lib.fk_lloyd(ctypes.byref(p), _ptr(X), _ptr(C), _ptr(labels), _ptr(counts),
@@ -235,3 +237,6 @@ def fk_baseline_update_scatter(X: torch.Tensor, labels: torch.Tensor, C_prev: to
                                           _ptr(C_next), _ptr(C_next_lowp), _ptr(counts),
                                           _ptr(sums), _stream(stream)),
            "fk_baseline_update_scatter")
+
+
+from .api import KMeans, batch_kmeans_euclid, initial_centroids  # noqa: E402  (uses the above)

@@ -62,6 +62,10 @@ Workspace workspace_layout(const fk_problem& p, char* base) {
     w.lowp = p.dtype == FK_F32 ? nullptr : take(B * K * d * (size_t)dtype_size(p.dtype));
     w.bad = reinterpret_cast<int32_t*>(take(B * sizeof(int32_t)));
     w.flags = reinterpret_cast<uint32_t*>(take(256));
+    w.psums = (p.flags & FK_DETERMINISTIC)
+                  ? reinterpret_cast<float*>(
+                        take(B * (size_t)piece_capacity(p.N, p.K) * d * sizeof(float)))
+                  : nullptr;
     w.total = o;
     return w;
 }
@@ -133,7 +137,7 @@ fk_status check_problem(const fk_problem* p) {
                     (long long)p->N, (long long)p->K, (long long)p->d);
     if (p->dtype != FK_F32 && p->dtype != FK_F16 && p->dtype != FK_BF16)
         return fail(FK_EUNSUPPORTED, "unknown dtype %d", (int)p->dtype);
-    if (p->reserved != 0) return fail(FK_EINVAL, "reserved field must be 0");
+    if (p->flags & ~FK_DETERMINISTIC) return fail(FK_EINVAL, "unknown flag bits 0x%x", (unsigned)p->flags);
     if (p->N > kMaxIndex || p->K > kMaxIndex)
         return fail(FK_EUNSUPPORTED, "N and K must be <= %lld", (long long)kMaxIndex);
     if (p->d > kMaxD) return fail(FK_EUNSUPPORTED, "d must be <= %lld", (long long)kMaxD);
@@ -158,6 +162,13 @@ fk_status check_ws(const fk_problem& p, void* ws, size_t ws_bytes, Workspace* ou
 }
 
 fk_status check_assign_d(const fk_problem&) { return FK_OK; }
+
+// FK_DETERMINISTIC needs the stable (tiled) argsort
+fk_status check_deterministic(const fk_problem& p) {
+    if ((p.flags & FK_DETERMINISTIC) && !sort_tiled(p.N, p.K))
+        return fail(FK_EUNSUPPORTED, "FK_DETERMINISTIC needs K <= 16000");
+    return FK_OK;
+}
 
 #define FK_CHECK(expr)                    \
     do {                                  \
@@ -217,6 +228,8 @@ fk_status fk_workspace_size(const fk_problem* p, int64_t chunk_points, size_t* b
     if (!bytes) return fail(FK_EINVAL, "bytes is NULL");
     if (chunk_points < 0) return fail(FK_EINVAL, "chunk_points must be >= 0");
     if (chunk_points > kMaxIndex) return fail(FK_EUNSUPPORTED, "chunk_points too large");
+    if (chunk_points > 0 && (p->flags & FK_DETERMINISTIC))
+        return fail(FK_EUNSUPPORTED, "FK_DETERMINISTIC is not available for the streamed path");
     *bytes = chunk_points == 0
                  ? workspace_layout(*p, nullptr).total
                  : stream_workspace_layout(*p, chunk_points < p->N ? chunk_points : p->N, nullptr).total;
@@ -272,6 +285,7 @@ fk_status fk_sort_labels(const fk_problem* p, const int32_t* labels, int32_t* co
     FK_CHECK(check_ptr(counts, "counts"));
     FK_CHECK(check_ptr(offsets, "offsets"));
     FK_CHECK(check_ptr(sorted_idx, "sorted_idx"));
+    FK_CHECK(check_deterministic(*p));
     Workspace w;
     FK_CHECK(check_ws(*p, ws, ws_bytes, &w));
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -291,13 +305,14 @@ fk_status fk_update(const fk_problem* p, const void* X, const int32_t* labels,
     if (p->dtype == FK_F32 && C_next_lowp && C_next_lowp == static_cast<void*>(C_next))
         return fail(FK_EINVAL, "C_next_lowp must differ from C_next");
     if (p->d > 1024) return fail(FK_EUNSUPPORTED, "update supports d <= 1024");
+    FK_CHECK(check_deterministic(*p));
     Workspace w;
     FK_CHECK(check_ws(*p, ws, ws_bytes, &w));
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t rows = p->B * p->K;
     FK_CHECK(enqueue_sort(*p, w, labels, counts, w.offsets, w.sorted_idx, true, nullptr, s));
-    SegParams sp{true, w.sums, w.arrive, C_prev, C_next,
-                 p->dtype == FK_F32 ? nullptr : C_next_lowp, nullptr, nullptr};
+    SegParams sp{true,    w.sums,  w.arrive, C_prev, C_next,
+                 p->dtype == FK_F32 ? nullptr : C_next_lowp, nullptr, nullptr, w.psums, w.poff};
     FK_TRY(launch_segment_sums(p->dtype, X, w.sorted_idx, w.offsets, w.pieces, sp, p->B, p->N,
                                p->K, (int)p->d, s),
            "segment sums");
@@ -320,6 +335,7 @@ fk_status fk_lloyd(const fk_problem* p, const void* X, float* C, int32_t* labels
     if (!(tol >= 0.f)) return fail(FK_EINVAL, "tol must be >= 0");
     FK_CHECK(check_assign_d(*p));
     if (p->d > 1024) return fail(FK_EUNSUPPORTED, "update supports d <= 1024");
+    FK_CHECK(check_deterministic(*p));
     Workspace w;
     FK_CHECK(check_ws(*p, ws, ws_bytes, &w));
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -329,7 +345,7 @@ fk_status fk_lloyd(const fk_problem* p, const void* X, float* C, int32_t* labels
 
     FK_TRY(launch_prepare(p->dtype, C, w.lowp, w.bias, rows, (int)p->d, s), "prepare centroids");
     uint32_t* move = sync ? w.flags + 1 : nullptr;
-    const SegParams sp{true, w.sums, w.arrive, C, C, w.lowp, w.bias, move};
+    const SegParams sp{true, w.sums, w.arrive, C, C, w.lowp, w.bias, move, w.psums, w.poff};
     int it = 0;
     while (it < max_iters) {
         FK_TRY(launch_assign(p->dtype, X, Cq, w.bias, labels, nullptr, p->B, p->N, p->K,
@@ -364,6 +380,8 @@ fk_status fk_lloyd_streamed(const fk_problem* p, const void* X_host, int64_t chu
     FK_CHECK(check_ptr(counts, "counts"));
     if (chunk_points < 1) return fail(FK_EINVAL, "chunk_points must be >= 1");
     if (chunk_points > kMaxIndex) return fail(FK_EUNSUPPORTED, "chunk_points too large");
+    if (p->flags & FK_DETERMINISTIC)
+        return fail(FK_EUNSUPPORTED, "FK_DETERMINISTIC is not available for the streamed path");
     if (max_iters < 1) return fail(FK_EINVAL, "max_iters must be >= 1");
     if (p->d > 1024) return fail(FK_EUNSUPPORTED, "update supports d <= 1024");
     const int64_t chunk = chunk_points < p->N ? chunk_points : p->N;

@@ -52,6 +52,7 @@ struct Workspace {
     void* lowp;          // [B][K][d] centroids in the problem dtype (16-bit dtypes)
     int32_t* bad;        // [B]      labels outside [0, K) per problem
     uint32_t* flags;     // [1] max squared move (fp32 bits)
+    float* psums;        // [B][piece_capacity][d] piece partial sums (FK_DETERMINISTIC), or null
     size_t total;
 };
 
@@ -105,6 +106,13 @@ struct SegParams {
     void* lowp;       // problem dtype, or null
     float* bias;      // or null
     uint32_t* move;   // or null
+    // final only: when set, the pieces of multi-piece segments store their
+    // partial sums here ([B][piece_capacity][d] fp32) instead of adding them
+    // with atomics, and a second pass adds them in piece order (a result
+    // that does not depend on timing); poff [B][K+1] = first piece of each
+    // segment
+    float* psums;
+    const int32_t* poff;
 };
 
 // ---- launchers (return hipSuccess or the launch error) ----------------------

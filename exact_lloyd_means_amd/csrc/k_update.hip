@@ -386,14 +386,19 @@ __global__ __launch_bounds__(kBlock) void k_plan(const int32_t* __restrict__ cou
     if (b == 0 && blk == 0 && threadIdx.x == 0 && move) *move = 0u;
 }
 
-// Scatter of tile t: base of label k = offsets[k] + th[b][t][k]; elements
-// are ranked with LDS atomics.  With sums the workgroups also clear the sum
-// rows of multi-piece segments.
+// Scatter of tile t: base of label k = offsets[k] + th[b][t][k].  The
+// scatter is stable: a label's points land in increasing index order.
+// Round j takes elements i0 + 256 j + tid (64 consecutive per wave); inside
+// a wave, the lanes holding the same label are found with one ballot per
+// label bit (nbits bits cover K - 1) and ranked by lane; across the waves
+// of a round each label's LDS base is advanced wave by wave, with a barrier
+// between, by the lowest lane of each group.  With sums the workgroups also
+// clear the sum rows of multi-piece segments.
 __global__ __launch_bounds__(kBlock) void k_tile_scatter(
     const int32_t* __restrict__ labels, const int32_t* __restrict__ th,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_idx,
     const int32_t* __restrict__ counts, float* __restrict__ sums, int32_t* __restrict__ arrive,
-    int64_t N, int64_t K, int64_t T, int64_t d, int xcd_map) {
+    int64_t N, int64_t K, int64_t T, int64_t d, int xcd_map, int nbits) {
     extern __shared__ int32_t s_base[];  // [K]
     // Workgroups go to the 8 XCDs round-robin.  With xcd_map (B a multiple
     // of 8, 1-D grid) all tiles of problem b run on XCD b mod 8, so the
@@ -422,10 +427,29 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(
         const int64_t i = i0 + threadIdx.x + j * kBlock;
         a[j] = i < i1 ? lab[i] : -1;
     }
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const uint64_t below = lane ? ~0ull >> (64 - lane) : 0ull;
 #pragma unroll
     for (int j = 0; j < kSortPer; ++j) {
         const int64_t i = i0 + threadIdx.x + j * kBlock;
-        if (a[j] >= 0 && a[j] < K) out[atomicAdd(&s_base[a[j]], 1)] = (int32_t)i;
+        const int32_t v = a[j];
+        const bool valid = v >= 0 && v < K;
+        uint64_t peers = __ballot(valid);
+        for (int bit = 0; bit < nbits; ++bit) {
+            const bool on = (v >> bit) & 1;
+            const uint64_t m = __ballot(on);
+            peers &= on ? m : ~m;
+        }
+        if (!valid) peers = 0;
+        const int rank = __popcll(peers & below);
+        int32_t base = 0;
+        for (int w = 0; w < kBlock / kWave; ++w) {
+            if (wave == w && valid && rank == 0) base = atomicAdd(&s_base[v], __popcll(peers));
+            __syncthreads();
+        }
+        base = __shfl(base, valid ? __ffsll((unsigned long long)peers) - 1 : lane);
+        if (valid) out[base + rank] = (int32_t)i;
     }
 }
 
@@ -595,6 +619,7 @@ struct SegOut {
     T* lowp;               // [B][K][d] or null
     float* bias;           // [B][K] or null
     uint32_t* move;        // max squared move (fp32 bits) or null
+    float* psums;          // [B][M][d] partial sums of pieces, or null (FINAL)
 };
 
 // Finalizes centroid row k of problem b from the lane's EPL sums.
@@ -746,6 +771,16 @@ __global__ __launch_bounds__(kBlock) void k_segment_sums(
         finalize_row<T, EPL, VEC>(o, b, K, d, k, count, acc, e0);
         return;
     }
+    if (FINAL && o.psums) {
+        // two-pass mode: the piece's partial sums for k_merge_pieces
+        if (active) {
+            float* pp = o.psums + (b * M + j) * d + e0;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+                if (VEC || e0 + e < d) pp[e] = acc[e];
+        }
+        return;
+    }
     float* dst = o.sums + (b * K + k) * d + e0;
     if constexpr (FINAL) {
         // Returning atomics: once their results are in, the adds are
@@ -776,6 +811,54 @@ __global__ __launch_bounds__(kBlock) void k_segment_sums(
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
             if (VEC || e0 + e < d) atomicAdd(dst + e, acc[e]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Second pass of the two-pass segment sums: one wave per segment of more
+// than one piece adds the pieces' partial sums in piece order (pieces
+// poff[k] .. poff[k] + npieces - 1 cover the segment front to back) and
+// finalizes the centroid as the fused path does.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_merge_pieces(const int32_t* __restrict__ offsets,
+                                                         const int32_t* __restrict__ poff,
+                                                         SegOut<T> o, int64_t K, int d, int64_t M) {
+    const int lane = threadIdx.x & 63;
+    const int64_t b = blockIdx.y;
+    const int64_t k = (int64_t)blockIdx.x * (kBlock / kWave) + (threadIdx.x >> 6);
+    if (k >= K) return;
+    const int32_t* off = offsets + b * (K + 1);
+    const int32_t count = off[k + 1] - off[k];
+    if (count <= kSegRun) return;
+    const int32_t np = npieces_of(count);
+    const int64_t j0 = poff[b * (K + 1) + k];
+    const float* ps = o.psums + (b * M + j0) * d;
+    const int64_t base = (b * K + k) * d;
+    const float fn = (float)count;
+    float cn = 0.f, mv = 0.f;
+    for (int j = lane; j < d; j += kWave) {
+        float sum = 0.f;
+        for (int32_t q = 0; q < np; ++q) sum += ps[(int64_t)q * d + j];
+        const float c = sum / fn;
+        const float prev = o.C_prev[base + j];
+        o.C_next[base + j] = c;
+        float cq = c;
+        if (o.lowp) {
+            const T q = (T)c;
+            o.lowp[base + j] = q;
+            cq = to_f32(q);
+        }
+        cn = fmaf(cq, cq, cn);
+        const float m = c - prev;
+        mv = fmaf(m, m, mv);
+    }
+    if (o.bias) {
+        cn = wave_sum(cn);
+        if (lane == 0) o.bias[b * K + k] = -0.5f * cn;
+    }
+    if (o.move) {
+        mv = wave_sum(mv);
+        if (lane == 0) atomicMax(o.move, __float_as_uint(mv));
     }
 }
 
@@ -837,8 +920,15 @@ hipError_t segment_sums_t(const void* X, const int32_t* sorted_idx, const int32_
     const int64_t row_wgs = sp.final ? (K + (kBlock / kWave) - 1) / (kBlock / kWave) : 0;
     const dim3 grid((unsigned)(piece_wgs + row_wgs), (unsigned)B);
     SegOut<T> o{sp.sums, sp.arrive, sp.C_prev, sp.C_next, static_cast<T*>(sp.lowp), sp.bias,
-                sp.move};
+                sp.move, sp.final ? sp.psums : nullptr};
     const T* x = static_cast<const T*>(X);
+    auto merge = [&](hipError_t e) {
+        if (e != hipSuccess || !o.psums) return e;
+        const dim3 mgrid((unsigned)((K + (kBlock / kWave) - 1) / (kBlock / kWave)), (unsigned)B);
+        hipLaunchKernelGGL((k_merge_pieces<T>), mgrid, dim3(kBlock), 0, s, offsets, sp.poff, o,
+                           K, d, M);
+        return hipGetLastError();
+    };
 #define FK_SEG_LAUNCH(E, V, F)                                                                 \
     hipLaunchKernelGGL((k_segment_sums<T, E, V, F>), grid, dim3(kBlock), 0, s, x, sorted_idx,  \
                        offsets, pieces, o, N, K, d, M, piece_wgs)
@@ -856,7 +946,7 @@ hipError_t segment_sums_t(const void* X, const int32_t* sorted_idx, const int32_
             else if (ld == 1) FK_SEG_LAUNCH(E, 1, false);                                      \
             else FK_SEG_LAUNCH(E, 0, false);                                                   \
         }                                                                                      \
-        return hipGetLastError();                                                              \
+        return merge(hipGetLastError());                                                       \
     }
     FK_SEG_CASE(1)
     FK_SEG_CASE(2)
@@ -962,9 +1052,10 @@ hipError_t launch_sort(const SortParams& sp, int64_t B, int64_t N, int64_t K, hi
     if (tiled) {
         const int xcd_map = B % 8 == 0 && T * B < ((int64_t)1 << 31);
         const dim3 sgrid = xcd_map ? dim3((unsigned)(T * B)) : tiles;
+        const int nbits = K > 1 ? 64 - __builtin_clzll((unsigned long long)(K - 1)) : 0;
         hipLaunchKernelGGL(k_tile_scatter, sgrid, dim3(kBlock), (size_t)K * sizeof(int32_t), s,
                            sp.labels, sp.table, sp.offsets, sp.sorted_idx, sp.counts, sp.sums,
-                           sp.arrive, N, K, T, sp.d, xcd_map);
+                           sp.arrive, N, K, T, sp.d, xcd_map, nbits);
     } else {
         const int64_t cb = min((K + kBlock - 1) / kBlock, (int64_t)256);
         hipLaunchKernelGGL(k_cursor, dim3((unsigned)cb, (unsigned)B), dim3(kBlock), 0, s,

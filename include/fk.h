@@ -73,11 +73,25 @@ typedef enum fk_status {
     FK_EHOST = -5
 } fk_status;
 
-/* Problem description shared by all calls.  dtype is an fk_dtype value. */
+/*
+ * Problem flags (fk_problem.flags, bitwise or; other bits must be 0).
+ *
+ * FK_DETERMINISTIC -- results of fk_update and fk_lloyd do not depend on
+ *   timing: the same inputs give the same bits on every run.  The argsort is
+ *   then stable, and segments longer than 256 points store each piece's
+ *   partial sums (workspace) and add them in piece order in a second pass
+ *   instead of with atomics.  Needs K <= 16000 (the tiled argsort; larger K
+ *   gives FK_EUNSUPPORTED) and is not available for fk_lloyd_streamed.  The
+ *   workspace grows by B * (ceil(N/256) + K) * d * 4 bytes.
+ */
+#define FK_DETERMINISTIC 1
+
+/* Problem description shared by all calls.  dtype is an fk_dtype value;
+ * flags a combination of the FK_* flags above (0: none). */
 typedef struct fk_problem {
     int64_t B, N, K, d;
     int32_t dtype;
-    int32_t reserved; /* must be 0 */
+    int32_t flags;
 } fk_problem;
 
 /* Version of this ABI (FK_ABI_VERSION of the built library). */
@@ -138,7 +152,8 @@ fk_status fk_assign_with_bias(const fk_problem* p, const void* X, const void* C,
  *                       number of labels in [0, K), N when all are valid);
  *   sorted_idx [B][N]   point indices grouped by label: positions
  *                       offsets[b][k] .. offsets[b][k+1]-1 hold the points of
- *                       label k, in unspecified order within the segment.
+ *                       label k, in increasing index order for K <= 16000
+ *                       (a stable argsort), in unspecified order otherwise.
  * Labels outside [0, K) are skipped and counted (fk_error_count).
  */
 fk_status fk_sort_labels(const fk_problem* p, const int32_t* labels, int32_t* counts,
@@ -158,9 +173,12 @@ fk_status fk_sort_labels(const fk_problem* p, const int32_t* labels, int32_t* co
  *   C_next_lowp [B][K][d] problem dtype = C_next rounded to nearest even,
  *     may be NULL (must be NULL or distinct from C_next for fp32);
  *   counts [B][K] int32.
- * For segments longer than 256 points the centroid low bits depend on the
- * order of the fp32 atomic additions and can differ between runs; counts
- * never do.  Labels outside [0, K) are skipped and counted (fk_error_count).
+ * The fp32 sums follow the sorted order within each segment (increasing
+ * point index for K <= 16000) and, for segments longer than 256 points, the
+ * order of the atomic additions of their pieces, so without FK_DETERMINISTIC
+ * the low bits of such centroids (and of every centroid for K > 16000) can
+ * differ between runs; with it they cannot.  Counts never differ.  Labels
+ * outside [0, K) are skipped and counted (fk_error_count).
  */
 fk_status fk_update(const fk_problem* p, const void* X, const int32_t* labels,
                     const float* C_prev, float* C_next, void* C_next_lowp, int32_t* counts,

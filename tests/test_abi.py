@@ -44,8 +44,8 @@ def test_status_strings():
     assert b"unknown" in fk.lib.fk_status_str(42)
 
 
-def P(B=2, N=100, K=10, d=16, dtype=fk.FK_F16, reserved=0):
-    return fk.Problem(B, N, K, d, dtype, reserved)
+def P(B=2, N=100, K=10, d=16, dtype=fk.FK_F16, flags=0):
+    return fk.Problem(B, N, K, d, dtype, flags)
 
 
 def ws_size(p):
@@ -75,8 +75,18 @@ def test_unknown_dtype_rejected():
     assert call_assign(P(dtype=7), ws_bytes=1 << 30) == fk.FK_EUNSUPPORTED
 
 
-def test_reserved_must_be_zero():
-    assert call_assign(P(reserved=1), ws_bytes=1 << 30) == fk.FK_EINVAL
+def test_deterministic_streamed_rejected():
+    p = P(flags=fk.FK_DETERMINISTIC)
+    n = ctypes.c_size_t(0)
+    assert fk.lib.fk_workspace_size(ctypes.byref(p), 0, ctypes.byref(n)) == fk.FK_OK
+    assert n.value > fk.workspace_size(P())
+    assert fk.lib.fk_workspace_size(ctypes.byref(p), 64, ctypes.byref(n)) == fk.FK_EUNSUPPORTED
+
+
+def test_unknown_flags_rejected():
+    assert call_assign(P(flags=2), ws_bytes=1 << 30) == fk.FK_EINVAL
+    assert b"flag" in fk.lib.fk_last_error()
+    assert call_assign(P(flags=fk.FK_DETERMINISTIC), ws_bytes=0) == fk.FK_EWORKSPACE
 
 
 @pytest.mark.parametrize("which", ["X", "C", "labels"])
