@@ -90,6 +90,10 @@ def main() -> int:
     ap.add_argument("--no-baselines", action="store_true",
                     help="skip timing the unfused baselines (materialised scores + argmin, "
                          "scatter-atomic update)")
+    ap.add_argument("--sweep-assign", action="store_true",
+                    help="time every shape of the fp16 assign kernel (fk_assign_variant) at "
+                         "B=32, N=65536, K=1024 and d = 64, 128, 256 against the library's "
+                         "own choice; prints one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB -> 1 GiB copy kernel (PMC byte-counter calibration)")
     ap.add_argument("--summarize", nargs="+", metavar="ARG",
@@ -113,6 +117,8 @@ def main() -> int:
     import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.sweep_assign:
+        return run_sweep(args)
     w = synth.CONFIGS[args.config]
     if args.config == 5:
         return run_streamed(args, w)
@@ -271,6 +277,91 @@ def main() -> int:
     }
     if pages_ms:
         out["baseline_context"] = f"pages: {pages_ms} ms/iter on NVIDIA H200 (FP16), not this machine"
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def run_sweep(args) -> int:
+    """Exhaustive sweep of the fp16 assign kernel's shapes (point blocks per
+    wave x waves per workgroup, then grid caps for the best shape) against
+    the shape fk_assign picks.  Every candidate is timed in each of several
+    rounds, in rotating order, and its median is reported, so clock and
+    power drift over the run do not favour any one shape."""
+    import itertools
+    import statistics
+
+    import torch
+
+    import exact_lloyd_means_amd as fk
+    import synth
+
+    reps, rounds = 5, 7
+    out = {"metric": "fp16 assign kernel time by shape, B=32 N=65536 K=1024", "unit": "ms",
+           "rows": [], "per_d": []}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        for _ in range(reps):
+            fn()
+        e[1].record()
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) / reps
+
+    def median_times(cands):
+        t = {c: [] for c in cands}
+        for r in range(rounds):
+            order = cands[r % len(cands):] + cands[:r % len(cands)]
+            for c in order:
+                t[c].append(timed(c[1]))
+        return {c: statistics.median(v) for c, v in t.items()}
+
+    for d in (64, 128, 256):
+        X, C0 = synth.make(2, d=d)
+        X = X.cuda()
+        B, N, _ = X.shape
+        K = C0.shape[1]
+        Cq = C0.cuda().to(X.dtype).contiguous()
+        bias = torch.empty((B, K), dtype=torch.float32, device="cuda")
+        fk.fk_centroid_bias(Cq, bias)
+        ref = torch.empty((B, N), dtype=torch.int32, device="cuda")
+        lab = torch.empty_like(ref)
+        flops = 2.0 * B * N * K * d
+        for _ in range(5):   # bring clocks to their loaded state
+            fk.fk_assign_with_bias(X, Cq, bias, ref)
+
+        def variant(np_, w, g=0):
+            return lambda: fk.fk_assign_variant(X, Cq, bias, lab, np_, w, g)
+        shapes = [((np_, w, 0), variant(np_, w)) for np_, w in itertools.product((1, 2, 4, 8),
+                                                                                   (4, 8))]
+        med = median_times(shapes)
+        best = min(shapes, key=lambda c: med[c])
+        grid = [((best[0][0], best[0][1], g), variant(best[0][0], best[0][1], g))
+                for g in (512, 1024, 2048)]
+        med.update(median_times(grid))
+        rows = []
+        for c in shapes + grid:
+            c[1]()
+            torch.cuda.synchronize()
+            np_, w, g = c[0]
+            rows.append({"d": d, "point_blocks": np_, "waves": w, "grid_wgs": g,
+                         "ms": round(med[c], 4), "TFLOPs": round(flops / med[c] / 1e9, 1),
+                         "labels_identical": bool(torch.equal(lab, ref))})
+            log(f"[sweep] d={d} np={np_} waves={w} grid={g}: {med[c]:.4f} ms")
+        # the shape fk_assign's dispatch picks (assign16_np and assign16_waves
+        # in k_assign16.inl: four blocks and four waves for d <= 128, two
+        # blocks and eight waves for d = 256), one launch per block of points
+        lib_shape = (4, 4, 0) if d <= 128 else (2, 8, 0)
+        lib_ms = med[next(c for c in shapes if c[0] == lib_shape)]
+        best_row = min(rows, key=lambda r: r["ms"])
+        out["rows"] += rows
+        out["per_d"].append({"d": d, "library_shape": {"point_blocks": lib_shape[0],
+                                                       "waves": lib_shape[1]},
+                             "library_choice_ms": round(lib_ms, 4), "best": best_row,
+                             "library_loss_pct": round(100.0 * (lib_ms / best_row["ms"] - 1), 2)})
+        del X
     print(json.dumps(out), flush=True)
     return 0
 

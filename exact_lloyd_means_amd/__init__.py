@@ -58,6 +58,9 @@ _SIG = {
     "fk_baseline_scores": ([_PP, _P, _P, _P, _P, _P], ctypes.c_int),
     "fk_baseline_argmin": ([_PP, _P, _P, _P], ctypes.c_int),
     "fk_baseline_update_scatter": ([_PP, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    # include/fk_tune.h
+    "fk_assign_variant": ([_PP, _P, _P, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int64, _P],
+                          ctypes.c_int),
 }
 for _name, (_args, _res) in _SIG.items():
     _fn = getattr(lib, _name)
@@ -238,5 +241,14 @@ def fk_baseline_update_scatter(X: torch.Tensor, labels: torch.Tensor, C_prev: to
                                           _ptr(sums), _stream(stream)),
            "fk_baseline_update_scatter")
 
+
+
+def fk_assign_variant(X: torch.Tensor, C: torch.Tensor, bias: torch.Tensor, labels: torch.Tensor,
+                      point_blocks: int, waves: int, grid_wgs: int = 0, stream=None) -> None:
+    """The fp16 fused assign with an explicit kernel shape (include/fk_tune.h)."""
+    p = _problem_from(X, C.shape[1])
+    _check(lib.fk_assign_variant(ctypes.byref(p), _ptr(X), _ptr(C), _ptr(bias), _ptr(labels),
+                                 int(point_blocks), int(waves), int(grid_wgs), _stream(stream)),
+           "fk_assign_variant")
 
 from .api import KMeans, batch_kmeans_euclid, initial_centroids  # noqa: E402  (uses the above)

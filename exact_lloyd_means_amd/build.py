@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libfk.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["fk_api.hip", "k_update.hip", "k_baseline.hip", "k_assign_f16.hip",
-           "k_assign_bf16.hip", "k_assign_f32.hip"]
+           "k_assign_bf16.hip", "k_assign_f32.hip", "k_tune.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

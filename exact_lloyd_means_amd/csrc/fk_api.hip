@@ -497,6 +497,31 @@ fk_status fk_error_count(const fk_problem* p, const void* ws, size_t ws_bytes, i
     return FK_OK;
 }
 
+// ---- tuning -------------------------------------------------------------------
+
+fk_status fk_assign_variant(const fk_problem* p, const void* X, const void* C, const float* bias,
+                            int32_t* labels, int point_blocks, int waves, int64_t grid_wgs,
+                            void* stream) {
+    FK_CHECK(check_problem(p));
+    FK_CHECK(check_ptr(X, "X"));
+    FK_CHECK(check_ptr(C, "C"));
+    FK_CHECK(check_ptr(bias, "bias"));
+    FK_CHECK(check_ptr(labels, "labels"));
+    if (p->dtype != FK_F16) return fail(FK_EUNSUPPORTED, "assign variants are fp16 only");
+    if (p->d != 64 && p->d != 128 && p->d != 256)
+        return fail(FK_EUNSUPPORTED, "assign variants need d = 64, 128 or 256");
+    if (p->K < 32) return fail(FK_EUNSUPPORTED, "assign variants need K >= 32");
+    if (point_blocks != 1 && point_blocks != 2 && point_blocks != 4 && point_blocks != 8)
+        return fail(FK_EINVAL, "point_blocks must be 1, 2, 4 or 8");
+    if (waves != 4 && waves != 8) return fail(FK_EINVAL, "waves must be 4 or 8");
+    if (grid_wgs < 0 || grid_wgs > 0x7fffffff) return fail(FK_EINVAL, "grid_wgs out of range");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    FK_TRY(launch_assign_variant(X, C, bias, labels, p->B, p->N, p->K, (int)p->d, point_blocks,
+                                 waves, grid_wgs, s),
+           "assign variant");
+    return FK_OK;
+}
+
 // ---- baselines ---------------------------------------------------------------
 
 fk_status fk_baseline_scores(const fk_problem* p, const void* X, const void* C, const float* bias,

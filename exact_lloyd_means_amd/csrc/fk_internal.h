@@ -7,6 +7,7 @@
 
 #include "../../include/fk.h"
 #include "../../include/fk_baseline.h"
+#include "../../include/fk_tune.h"
 
 namespace fk {
 
@@ -145,6 +146,11 @@ hipError_t launch_segment_sums(int dtype, const void* X, const int32_t* sorted_i
 hipError_t launch_finalize(int dtype, float* sums, const int32_t* counts, const float* C_prev,
                            float* C_next, void* lowp, float* bias, uint32_t* move_max,
                            int64_t rows, int d, hipStream_t s);
+
+// fp16 fused assign with an explicit shape (d = 64, 128 or 256)
+hipError_t launch_assign_variant(const void* X, const void* C, const float* bias, int32_t* labels,
+                                 int64_t B, int64_t N, int64_t K, int d, int np, int waves,
+                                 int64_t grid_wgs, hipStream_t s);
 
 // ---- baselines: materialised scores + argmin, scatter-atomic update --------
 // D [B][N][K] fp32 = x.c + bias for 16-bit inputs with d <= 256.

@@ -52,7 +52,7 @@ struct Mfma16<__bf16> {
 // NP point blocks.  Staging (registers -> ring of four LDS buffers), the
 // prefetch of the next tile's fragments and bias, and the branch-free
 // overlapping last tile are those of k_assign.
-template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK, bool MAT>
+template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK, bool MAT, int W>
 __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* __restrict__ C,
                                               const float* __restrict__ bias,
                                               int32_t* __restrict__ labels,
@@ -65,9 +65,9 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
     constexpr int ROWB = RC * 16 + 16;                 // LDS bytes per centroid row (padded)
     constexpr int TILEB = kAssignBK * ROWB;
     constexpr int CHUNKS = kAssignBK * RC;             // 16-byte chunks per centroid tile
-    constexpr int NT = kAssignWaves * kWave;
+    constexpr int NT = W * kWave;
     constexpr int PER = (CHUNKS + NT - 1) / NT;
-    constexpr int PTS = kAssignWaves * NP * 16;        // points per item
+    constexpr int PTS = W * NP * 16;                   // points per item
     constexpr int RB = 2;                              // row blocks per tile
     constexpr int kSlots = S * RB;
     constexpr int P = kSlots <= 2 ? kSlots : 2;        // fragments prefetched for the next tile
@@ -365,13 +365,13 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
     }
 }
 
-template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK>
-__global__ __launch_bounds__(kAssignWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK, int W = kAssignWaves>
+__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_assign16(const T* __restrict__ X, const T* __restrict__ C, const float* __restrict__ bias,
                 int32_t* __restrict__ labels, float* __restrict__ min_dist, int64_t B, int64_t N,
                 int64_t K, int d) {
-    assign16_body<T, S, NP, VEC, EXACT, SMALLK, false>(X, C, bias, labels, min_dist, B, N, K, d,
-                                                       nullptr);
+    assign16_body<T, S, NP, VEC, EXACT, SMALLK, false, W>(X, C, bias, labels, min_dist, B, N, K,
+                                                          d, nullptr);
 }
 
 // The same contraction writing every score (MAT) instead of the argmax.
@@ -379,67 +379,101 @@ template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK>
 __global__ __launch_bounds__(kAssignWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_scores16(const T* __restrict__ X, const T* __restrict__ C, const float* __restrict__ bias,
                 float* __restrict__ D, int64_t B, int64_t N, int64_t K, int d) {
-    assign16_body<T, S, NP, VEC, EXACT, SMALLK, true>(X, C, bias, nullptr, nullptr, B, N, K, d, D);
+    assign16_body<T, S, NP, VEC, EXACT, SMALLK, true, kAssignWaves>(X, C, bias, nullptr, nullptr,
+                                                                    B, N, K, d, D);
 }
 
-template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK, bool MAT = false>
+// Launch of one instantiation.  W = waves per workgroup; grid_wgs > 0 caps
+// the grid at that many workgroups (each then loops over several items).
+template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK, bool MAT = false,
+          int W = kAssignWaves>
 hipError_t launch_assign16_t(const void* X, const void* C, const float* bias, int32_t* labels,
                              float* min_dist, int64_t B, int64_t N, int64_t K, int d,
-                             hipStream_t s, float* D = nullptr) {
+                             hipStream_t s, float* D = nullptr, int64_t grid_wgs = 0) {
+    static_assert(!MAT || W == kAssignWaves, "scores mode uses the default shape");
     constexpr int lds = kAssignRing * (kAssignBK * (4 * S * 16 + 16) + kAssignBK * 4);
     static_assert(lds <= kLdsBytes, "LDS budget");
-    constexpr int PTS = kAssignWaves * NP * 16;
+    constexpr int PTS = W * NP * 16;
     const void* kern;
     if constexpr (MAT)
         kern = reinterpret_cast<const void*>(k_scores16<T, S, NP, VEC, EXACT, SMALLK>);
     else
-        kern = reinterpret_cast<const void*>(k_assign16<T, S, NP, VEC, EXACT, SMALLK>);
+        kern = reinterpret_cast<const void*>(k_assign16<T, S, NP, VEC, EXACT, SMALLK, W>);
     static bool attr_set = false;  // one attribute call per instantiation and process
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const dim3 grid((unsigned)(B * ((N + PTS - 1) / PTS)));
+    const int64_t items = B * ((N + PTS - 1) / PTS);
+    const dim3 grid((unsigned)(grid_wgs > 0 && grid_wgs < items ? grid_wgs : items));
     if constexpr (MAT)
         hipLaunchKernelGGL((k_scores16<T, S, NP, VEC, EXACT, SMALLK>), grid,
                            dim3(kAssignWaves * kWave), lds, s, static_cast<const T*>(X),
                            static_cast<const T*>(C), bias, D, B, N, K, d);
     else
-        hipLaunchKernelGGL((k_assign16<T, S, NP, VEC, EXACT, SMALLK>), grid,
-                           dim3(kAssignWaves * kWave), lds, s, static_cast<const T*>(X),
-                           static_cast<const T*>(C), bias, labels, min_dist, B, N, K, d);
+        hipLaunchKernelGGL((k_assign16<T, S, NP, VEC, EXACT, SMALLK, W>), grid, dim3(W * kWave),
+                           lds, s, static_cast<const T*>(X), static_cast<const T*>(C), bias,
+                           labels, min_dist, B, N, K, d);
     return hipGetLastError();
 }
 
+// Estimated VGPRs per lane of k_assign16 with S k-steps and NP point
+// blocks: the points' fragments (4 S NP), two accumulator sets of two row
+// blocks (16 NP), one tile's centroid fragments (8 S), running and per-tile
+// (score, index) pairs (8 NP), and staging, prefetch, bias and addresses
+// (about 40).
+constexpr int assign16_vgprs(int S, int NP) {
+    return 4 * S * NP + 16 * NP + 8 * S + 8 * NP + 40;
+}
+
+// Point blocks per wave: the most (a power of two up to 8) whose estimate
+// fits the 256 VGPRs a lane has at two waves per SIMD.  Each centroid
+// fragment read from LDS feeds NP matrix instructions, so more is better
+// until registers spill.  Gives 4 for S <= 4 and 2 for S = 8.
+constexpr int assign16_np(int S) {
+    return assign16_vgprs(S, 8) <= 256   ? 8
+           : assign16_vgprs(S, 4) <= 256 ? 4
+           : assign16_vgprs(S, 2) <= 256 ? 2
+                                         : 1;
+}
+
+// Waves per workgroup: four (two workgroups per CU, each with its own LDS
+// ring, so one workgroup's barrier waits overlap the other's matrix work)
+// while a workgroup still stages each centroid tile for at least 256
+// points; otherwise eight (one workgroup per CU).  Gives 4 for S <= 4 and
+// 8 for S = 8.
+constexpr int assign16_waves(int S) { return 4 * assign16_np(S) * 16 >= 256 ? 4 : 8; }
+
 // 16-bit inputs with d <= 256: S = k-steps of 32 (a power of two covering
-// d), four 16-point blocks per wave (two for S = 8).
+// d), assign16_np(S) 16-point blocks per wave, assign16_waves(S) waves.
 template <typename T>
 hipError_t dispatch_assign16(const void* X, const void* C, const float* bias, int32_t* labels,
                              float* min_dist, int64_t B, int64_t N, int64_t K, int d,
                              hipStream_t s) {
     const int need = (d + 31) / 32;
     const bool vec = (d % 8) == 0;
-#define FK_ASSIGN16_CASE(SS, NPP)                                                              \
+#define FK_ASSIGN16_CASE(SS)                                                                   \
     if (need <= SS) {                                                                          \
+        constexpr int NPP = assign16_np(SS), WW = assign16_waves(SS);                          \
         if (K < kAssignBK)                                                                     \
-            return vec ? launch_assign16_t<T, SS, NPP, true, false, true>(                     \
+            return vec ? launch_assign16_t<T, SS, NPP, true, false, true, false, WW>(          \
                              X, C, bias, labels, min_dist, B, N, K, d, s)                      \
-                       : launch_assign16_t<T, SS, NPP, false, false, true>(                    \
+                       : launch_assign16_t<T, SS, NPP, false, false, true, false, WW>(         \
                              X, C, bias, labels, min_dist, B, N, K, d, s);                     \
         if (vec && d == 32 * SS)                                                               \
-            return launch_assign16_t<T, SS, NPP, true, true, false>(X, C, bias, labels,        \
-                                                                    min_dist, B, N, K, d, s);  \
+            return launch_assign16_t<T, SS, NPP, true, true, false, false, WW>(                \
+                X, C, bias, labels, min_dist, B, N, K, d, s);                                  \
         if (vec)                                                                               \
-            return launch_assign16_t<T, SS, NPP, true, false, false>(X, C, bias, labels,       \
-                                                                     min_dist, B, N, K, d, s); \
-        return launch_assign16_t<T, SS, NPP, false, false, false>(X, C, bias, labels, min_dist, \
-                                                                  B, N, K, d, s);              \
+            return launch_assign16_t<T, SS, NPP, true, false, false, false, WW>(               \
+                X, C, bias, labels, min_dist, B, N, K, d, s);                                  \
+        return launch_assign16_t<T, SS, NPP, false, false, false, false, WW>(                  \
+            X, C, bias, labels, min_dist, B, N, K, d, s);                                      \
     }
-    FK_ASSIGN16_CASE(1, 4)
-    FK_ASSIGN16_CASE(2, 4)
-    FK_ASSIGN16_CASE(4, 4)
-    FK_ASSIGN16_CASE(8, 2)
+    FK_ASSIGN16_CASE(1)
+    FK_ASSIGN16_CASE(2)
+    FK_ASSIGN16_CASE(4)
+    FK_ASSIGN16_CASE(8)
 #undef FK_ASSIGN16_CASE
     return hipErrorInvalidValue;
 }
@@ -463,13 +497,18 @@ hipError_t dispatch_scores16(const void* X, const void* C, const float* bias, fl
                    : launch_assign16_t<T, SS, NPP, false, false, false, true>(                   \
                          X, C, bias, nullptr, nullptr, B, N, K, d, s, D);                        \
     }
-    FK_SCORES16_CASE(1, 4)
-    FK_SCORES16_CASE(2, 4)
-    FK_SCORES16_CASE(4, 4)
-    FK_SCORES16_CASE(8, 2)
+    FK_SCORES16_CASE(1, assign16_np(1))
+    FK_SCORES16_CASE(2, assign16_np(2))
+    FK_SCORES16_CASE(4, assign16_np(4))
+    FK_SCORES16_CASE(8, assign16_np(8))
 #undef FK_SCORES16_CASE
     return hipErrorInvalidValue;
 }
+
+static_assert(assign16_np(1) == 4 && assign16_np(2) == 4 && assign16_np(4) == 4 &&
+                  assign16_np(8) == 2,
+              "point blocks per wave");
+static_assert(assign16_waves(4) == 4 && assign16_waves(8) == 8, "waves per workgroup");
 
 }  // namespace
 }  // namespace fk

@@ -155,6 +155,20 @@ def test_baseline_validation():
     assert b"differ" in lib.fk_last_error()
 
 
+def test_assign_variant_validation():
+    lib = fk.lib
+
+    def call(p, np_=4, waves=8, grid=0):
+        return lib.fk_assign_variant(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, np_, waves, grid,
+                                     None)
+    assert call(P(d=128, K=64, dtype=fk.FK_F32)) == fk.FK_EUNSUPPORTED
+    assert call(P(d=100, K=64)) == fk.FK_EUNSUPPORTED
+    assert call(P(d=128, K=16)) == fk.FK_EUNSUPPORTED
+    assert call(P(d=128, K=64), np_=3) == fk.FK_EINVAL
+    assert call(P(d=128, K=64), waves=6) == fk.FK_EINVAL
+    assert call(P(d=128, K=64), grid=-1) == fk.FK_EINVAL
+
+
 def test_workspace_has_no_NK_term():
     """Workspace grows with B*N, B*K*d and B*K only (no distance matrix)."""
     def size(B, N, K, d):
