@@ -73,7 +73,7 @@ def batch_kmeans_euclid(X: torch.Tensor, n_clusters: int, max_iter: int = 100, t
     """Exact Lloyd k-means on each of the B problems of X (B, N, d).
 
     deterministic: the library's FK_DETERMINISTIC mode (bit-identical results
-    on every run; K <= 16000).  Returns (labels (B, N) int32 of the last
+    on every run).  Returns (labels (B, N) int32 of the last
     assignment, centroids (B, K, d) fp32 after the last update, number of
     iterations run)."""
     Xb, _ = _as_batched(X)

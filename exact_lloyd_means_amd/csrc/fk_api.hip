@@ -51,6 +51,9 @@ Workspace workspace_layout(const fk_problem& p, char* base) {
     w.bias = reinterpret_cast<float*>(take(B * K * sizeof(float)));
     w.offsets = reinterpret_cast<int32_t*>(take(B * (K + 1) * sizeof(int32_t)));
     w.table = reinterpret_cast<int32_t*>(take(B * tab * sizeof(int32_t)));
+    w.radix = reinterpret_cast<int32_t*>(
+        take(B * (size_t)radix_pairs_bound(p.N, p.K) * sizeof(int32_t)));
+    w.nvalid = reinterpret_cast<int32_t*>(take(B * sizeof(int32_t)));
     w.sorted_idx = reinterpret_cast<int32_t*>(take(B * N * sizeof(int32_t)));
     w.poff = reinterpret_cast<int32_t*>(take(B * (K + 1) * sizeof(int32_t)));
     w.pieces = reinterpret_cast<int32_t*>(
@@ -88,6 +91,9 @@ StreamWorkspace stream_workspace_layout(const fk_problem& p, int64_t chunk, char
     w.ccounts = reinterpret_cast<int32_t*>(take(K * sizeof(int32_t)));
     w.offsets = reinterpret_cast<int32_t*>(take((K + 1) * sizeof(int32_t)));
     w.table = reinterpret_cast<int32_t*>(take((size_t)sort_table_bound(chunk, p.K) * sizeof(int32_t)));
+    w.radix = reinterpret_cast<int32_t*>(
+        take((size_t)radix_pairs_bound(chunk, p.K) * sizeof(int32_t)));
+    w.nvalid = reinterpret_cast<int32_t*>(take(256));
     w.sorted_idx = reinterpret_cast<int32_t*>(take(c * sizeof(int32_t)));
     w.poff = reinterpret_cast<int32_t*>(take((K + 1) * sizeof(int32_t)));
     w.pieces = reinterpret_cast<int32_t*>(
@@ -163,12 +169,8 @@ fk_status check_ws(const fk_problem& p, void* ws, size_t ws_bytes, Workspace* ou
 
 fk_status check_assign_d(const fk_problem&) { return FK_OK; }
 
-// FK_DETERMINISTIC needs the stable (tiled) argsort
-fk_status check_deterministic(const fk_problem& p) {
-    if ((p.flags & FK_DETERMINISTIC) && !sort_tiled(p.N, p.K))
-        return fail(FK_EUNSUPPORTED, "FK_DETERMINISTIC needs K <= 16000");
-    return FK_OK;
-}
+// FK_DETERMINISTIC: every argsort is stable; nothing to check beyond flags
+fk_status check_deterministic(const fk_problem&) { return FK_OK; }
 
 #define FK_CHECK(expr)                    \
     do {                                  \
@@ -192,6 +194,8 @@ fk_status enqueue_sort(const fk_problem& p, const Workspace& w, const int32_t* l
     sp.pieces = w.pieces;
     sp.part = w.part;
     sp.table = w.table;
+    sp.radix = w.radix;
+    sp.nvalid = w.nvalid;
     sp.bad = w.bad;
     sp.move = move;
     if (clear_update) {
@@ -452,6 +456,8 @@ fk_status fk_lloyd_streamed(const fk_problem* p, const void* X_host, int64_t chu
                     so.pieces = w.pieces;
                     so.part = w.part;
                     so.table = w.table;
+                    so.radix = w.radix;
+                    so.nvalid = w.nvalid;
                     so.bad = w.bad;
                     FK_TRY(launch_sort(so, 1, n, K, cs), "sort chunk labels");
                     const SegParams sp{false, w.sums + b * K * d, nullptr, nullptr, nullptr,

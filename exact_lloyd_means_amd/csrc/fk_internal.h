@@ -37,12 +37,18 @@ bool sort_tiled(int64_t N, int64_t K);
 // upper bound for every N' <= N
 int64_t sort_table_bound(int64_t N, int64_t K);
 
+// int32 entries per problem of the radix sort's (label, point) pair buffers
+// (0 when the tiled sort applies)
+int64_t radix_pairs_bound(int64_t N, int64_t K);
+
 // Workspace layout.  Every region starts on a 256-byte boundary.  Sizes grow
 // with B*K*d, B*N and B*K only: the N x K distance matrix has no place here.
 struct Workspace {
     float* bias;         // [B][K]   -0.5 |c|^2 of the centroids an assign reads
     int32_t* offsets;    // [B][K+1] segment starts of the sorted labels
-    int32_t* table;      // [B][sort_table_bound] per-tile counts or cursors
+    int32_t* table;      // [B][sort_table_bound] per-tile label or digit counts
+    int32_t* radix;      // [B][radix_pairs_bound] pair buffers of the radix sort
+    int32_t* nvalid;     // [B]      valid labels (radix sort)
     int32_t* sorted_idx; // [B][N]   argsort of the labels
     int32_t* poff;       // [B][K+1] first piece of each segment
     int32_t* pieces;     // [B][1 + 2 * piece_capacity] piece count, segments, starts
@@ -69,6 +75,8 @@ struct StreamWorkspace {
     int32_t* ccounts;    // [K]   counts of one chunk
     int32_t* offsets;    // [K+1] segment starts of one chunk
     int32_t* table;      // [sort_table_bound(chunk)]
+    int32_t* radix;      // [radix_pairs_bound(chunk)]
+    int32_t* nvalid;     // [1]
     int32_t* sorted_idx; // [chunk]
     int32_t* poff;       // [K+1]
     int32_t* pieces;     // [1 + 2 * piece_capacity(chunk)]
@@ -88,6 +96,8 @@ struct SortParams {
     int32_t* poff;          // [B][K+1]
     int32_t* pieces;        // [B][1 + 2 * piece_capacity]
     int32_t* table;         // [B][sort_table_bound]
+    int32_t* radix;         // [B][radix_pairs_bound] (radix sort only)
+    int32_t* nvalid;        // [B] (radix sort only)
     int32_t* bad;           // [B]
     uint32_t* move;         // cleared when not null
     float* sums;            // [B][K][d] rows of multi-piece segments cleared (or null)

@@ -494,55 +494,163 @@ __global__ __launch_bounds__(kBlock) void k_histogram(const int32_t* __restrict_
     if (nbad) atomicAdd(&bad[b], nbad);
 }
 
-// cursor = offsets (global-atomic scatter)
-__global__ void k_cursor(const int32_t* __restrict__ offsets, int32_t* __restrict__ cursor,
-                         int64_t K) {
-    const int64_t b = blockIdx.y;
-    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < K;
-         k += (int64_t)gridDim.x * blockDim.x)
-        cursor[b * K + k] = offsets[b * (K + 1) + k];
+// ---- radix argsort (K above the tiled sort's limit) ---------------------------
+// A least-significant-digit radix sort of the valid labels by 8-bit digits,
+// each pass a stable counting sort of (label, point) pairs, so the result
+// is the stable argsort for any K.  Pass 0 reads the labels (skipping those
+// outside [0, K)) with the point index as value; later passes read the
+// previous pass's pairs, of which there are nvalid[b].
+constexpr int kDigits = 256;
+
+// dth[b][t][r] = #{elements of tile t whose digit is r}
+__global__ __launch_bounds__(kBlock) void k_digit_hist(const int32_t* __restrict__ keys,
+                                                       int64_t key_stride, int64_t N, int64_t K,
+                                                       int first,
+                                                       const int32_t* __restrict__ nvalid,
+                                                       int shift, int32_t* __restrict__ dth,
+                                                       int64_t T) {
+    __shared__ int32_t s_h[kDigits];
+    const int64_t b = blockIdx.y, t = blockIdx.x;
+    s_h[threadIdx.x] = 0;
+    __syncthreads();
+    const int64_t n = first ? N : nvalid[b];
+    const int64_t i0 = t * kSortTile;
+    const int64_t i1 = min(i0 + (int64_t)kSortTile, n);
+    const int32_t* kin = keys + b * key_stride;
+    int32_t a[kSortPer];
+#pragma unroll
+    for (int j = 0; j < kSortPer; ++j) {
+        const int64_t i = i0 + threadIdx.x + j * kBlock;
+        a[j] = i < i1 ? kin[i] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kSortPer; ++j) {
+        const int64_t i = i0 + threadIdx.x + j * kBlock;
+        if (i < i1 && a[j] >= 0 && a[j] < K) atomicAdd(&s_h[(a[j] >> shift) & (kDigits - 1)], 1);
+    }
+    __syncthreads();
+    dth[(b * T + t) * kDigits + threadIdx.x] = s_h[threadIdx.x];
 }
 
-// sorted_idx[b][pos] = i with pos inside label a_i's segment
-__global__ __launch_bounds__(kBlock) void k_scatter(const int32_t* __restrict__ labels,
-                                                    int32_t* __restrict__ cursor,
-                                                    int32_t* __restrict__ sorted_idx,
-                                                    const int32_t* __restrict__ counts,
-                                                    float* __restrict__ sums,
-                                                    int32_t* __restrict__ arrive, int64_t N,
-                                                    int64_t K, int64_t d, int use_lds) {
-    extern __shared__ int32_t s_base[];
-    const int64_t b = blockIdx.y;
-    if (sums)
-        clear_multi_rows(counts + b * K, sums + b * K * d, arrive + b * K, K, d, blockIdx.x,
-                         gridDim.x);
-    const int64_t i0 = (int64_t)blockIdx.x * kSortTile;
-    const int64_t i1 = min(i0 + (int64_t)kSortTile, N);
-    const int32_t* lab = labels + b * N;
-    int32_t* cur = cursor + b * K;
-    int32_t* out = sorted_idx + b * N;
-    if (use_lds) {
-        for (int64_t k = threadIdx.x; k < K; k += kBlock) s_base[k] = 0;
+// dth[b][t][r] <- (elements of digit < r) + (elements of digit r in tiles
+// < t): the output base of each tile and digit; nvalid[b] = total.  One
+// workgroup of 4 x 256 threads per problem: thread (g, r) takes digit r over
+// the g-th quarter of the tiles.
+constexpr int kDigitGroups = 4;
+__global__ __launch_bounds__(kDigits * kDigitGroups) void k_digit_colscan(
+    int32_t* __restrict__ dth, int32_t* __restrict__ nvalid, int64_t T) {
+    __shared__ int32_t s_tot[kDigitGroups][kDigits];
+    __shared__ int32_t s_scan[kDigits];
+    const int64_t b = blockIdx.x;
+    const int r = threadIdx.x & (kDigits - 1);
+    const int g = threadIdx.x / kDigits;
+    const int64_t per = (T + kDigitGroups - 1) / kDigitGroups;
+    const int64_t t0 = min(g * per, T), t1 = min(t0 + per, T);
+    int32_t* col = dth + b * T * kDigits + r;
+    int32_t sum = 0;
+    int64_t t = t0;
+    for (; t + 8 <= t1; t += 8) {
+        int32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = col[(t + u) * kDigits];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += v[u];
+    }
+    for (; t < t1; ++t) sum += col[t * kDigits];
+    s_tot[g][r] = sum;
+    __syncthreads();
+    int32_t run = 0, total = 0;
+#pragma unroll
+    for (int q = 0; q < kDigitGroups; ++q) {
+        run += q < g ? s_tot[q][r] : 0;
+        total += s_tot[q][r];
+    }
+    // inclusive scan of the digit totals (Hillis-Steele over 256 entries)
+    if (g == 0) s_scan[r] = total;
+    __syncthreads();
+    for (int off = 1; off < kDigits; off <<= 1) {
+        const int32_t v = (g == 0 && r >= off) ? s_scan[r - off] : 0;
         __syncthreads();
-        for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
-            const int32_t a = lab[i];
-            if (a >= 0 && a < K) atomicAdd(&s_base[a], 1);
-        }
+        if (g == 0) s_scan[r] += v;
         __syncthreads();
-        // one global reservation per label present in this tile
-        for (int64_t k = threadIdx.x; k < K; k += kBlock) {
-            const int32_t v = s_base[k];
-            if (v) s_base[k] = atomicAdd(&cur[k], v);
+    }
+    run += s_scan[r] - total;
+    if (threadIdx.x == 0) nvalid[b] = s_scan[kDigits - 1];
+    t = t0;
+    for (; t + 8 <= t1; t += 8) {
+        int32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = col[(t + u) * kDigits];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            col[(t + u) * kDigits] = run;
+            run += v[u];
         }
-        __syncthreads();
-        for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
-            const int32_t a = lab[i];
-            if (a >= 0 && a < K) out[atomicAdd(&s_base[a], 1)] = (int32_t)i;
+    }
+    for (; t < t1; ++t) {
+        const int32_t v = col[t * kDigits];
+        col[t * kDigits] = run;
+        run += v;
+    }
+}
+
+// Stable scatter of one pass: element i of tile t goes to
+// dth[b][t][digit] + (its rank among the tile's elements of that digit, in
+// index order), ranked as in k_tile_scatter (ballots over the 8 digit bits,
+// then wave by wave).  keys_out may be null (last pass: values only).  With
+// sums the workgroups also clear the sum rows of multi-piece segments.
+__global__ __launch_bounds__(kBlock) void k_digit_scatter(
+    const int32_t* __restrict__ keys, const int32_t* __restrict__ vals, int64_t in_stride,
+    int64_t N, int64_t K, int first, const int32_t* __restrict__ nvalid, int shift,
+    const int32_t* __restrict__ dth, int64_t T, int32_t* __restrict__ keys_out,
+    int32_t* __restrict__ vals_out, int64_t out_stride, const int32_t* __restrict__ counts,
+    float* __restrict__ sums, int32_t* __restrict__ arrive, int64_t d) {
+    __shared__ int32_t s_base[kDigits];
+    const int64_t b = blockIdx.y, t = blockIdx.x;
+    if (sums) clear_multi_rows(counts + b * K, sums + b * K * d, arrive + b * K, K, d, t, T);
+    s_base[threadIdx.x] = dth[(b * T + t) * kDigits + threadIdx.x];
+    __syncthreads();
+    const int64_t n = first ? N : nvalid[b];
+    const int64_t i0 = t * kSortTile;
+    const int64_t i1 = min(i0 + (int64_t)kSortTile, n);
+    const int32_t* kin = keys + b * in_stride;
+    const int32_t* vin = vals ? vals + b * in_stride : nullptr;
+    int32_t* kout = keys_out ? keys_out + b * out_stride : nullptr;
+    int32_t* vout = vals_out + b * out_stride;
+    int32_t a[kSortPer], v[kSortPer];
+#pragma unroll
+    for (int j = 0; j < kSortPer; ++j) {
+        const int64_t i = i0 + threadIdx.x + j * kBlock;
+        a[j] = i < i1 ? kin[i] : -1;
+        v[j] = vin ? (i < i1 ? vin[i] : 0) : (int32_t)i;
+    }
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const uint64_t below = lane ? ~0ull >> (64 - lane) : 0ull;
+#pragma unroll
+    for (int j = 0; j < kSortPer; ++j) {
+        const int64_t i = i0 + threadIdx.x + j * kBlock;
+        const bool valid = i < i1 && a[j] >= 0 && a[j] < K;
+        const int32_t dig = (a[j] >> shift) & (kDigits - 1);
+        uint64_t peers = __ballot(valid);
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+            const bool on = (dig >> bit) & 1;
+            const uint64_t m = __ballot(on);
+            peers &= on ? m : ~m;
         }
-    } else {
-        for (int64_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
-            const int32_t a = lab[i];
-            if (a >= 0 && a < K) out[atomicAdd(&cur[a], 1)] = (int32_t)i;
+        if (!valid) peers = 0;
+        const int rank = __popcll(peers & below);
+        int32_t base = 0;
+        for (int w = 0; w < kBlock / kWave; ++w) {
+            if (wave == w && valid && rank == 0) base = atomicAdd(&s_base[dig], __popcll(peers));
+            __syncthreads();
+        }
+        base = __shfl(base, valid ? __ffsll((unsigned long long)peers) - 1 : lane);
+        if (valid) {
+            const int32_t pos = base + rank;
+            if (kout) kout[pos] = a[j];
+            vout[pos] = v[j];
         }
     }
 }
@@ -968,8 +1076,16 @@ bool sort_tiled(int64_t N, int64_t K) {
 
 int64_t sort_table_bound(int64_t N, int64_t K) {
     const int64_t T = (N + kSortTile - 1) / kSortTile;
-    const int64_t tiled = min(T * (K + 1), 4 * N + 65536);
-    return tiled > K ? tiled : K;
+    if (sort_tiled(N, K)) return T * (K + 1);
+    return T * kDigits;  // radix passes: per-tile digit counts
+}
+
+int64_t radix_pairs_bound(int64_t N, int64_t K) { return sort_tiled(N, K) ? 0 : 4 * N; }
+
+int radix_passes(int64_t K) {
+    int bits = 0;
+    while (bits < 31 && ((int64_t)1 << bits) < K) ++bits;  // labels < 2^bits
+    return bits <= 8 ? 1 : (bits + 7) / 8;
 }
 
 hipError_t launch_fill_u32(uint32_t* ptr, int64_t n, uint32_t value, hipStream_t s) {
@@ -1057,11 +1173,26 @@ hipError_t launch_sort(const SortParams& sp, int64_t B, int64_t N, int64_t K, hi
                            sp.labels, sp.table, sp.offsets, sp.sorted_idx, sp.counts, sp.sums,
                            sp.arrive, N, K, T, sp.d, xcd_map, nbits);
     } else {
-        const int64_t cb = min((K + kBlock - 1) / kBlock, (int64_t)256);
-        hipLaunchKernelGGL(k_cursor, dim3((unsigned)cb, (unsigned)B), dim3(kBlock), 0, s,
-                           sp.offsets, sp.table, K);
-        hipLaunchKernelGGL(k_scatter, tiles, dim3(kBlock), lds, s, sp.labels, sp.table,
-                           sp.sorted_idx, sp.counts, sp.sums, sp.arrive, N, K, sp.d, use_lds);
+        // LSD radix passes over 8-bit digits; pairs ping-pong between the
+        // two halves of the radix buffer, the last pass writes sorted_idx
+        const int np = radix_passes(K);
+        const int64_t RP = radix_pairs_bound(N, K);
+        for (int q = 0; q < np; ++q) {
+            const bool first = q == 0, last = q == np - 1;
+            const int32_t* kin = first ? sp.labels : sp.radix + ((q - 1) % 2) * 2 * N;
+            const int32_t* vin = first ? nullptr : kin + N;
+            const int64_t in_stride = first ? N : RP;
+            int32_t* kout = last ? nullptr : sp.radix + (q % 2) * 2 * N;
+            int32_t* vout = last ? sp.sorted_idx : kout + N;
+            const int64_t out_stride = last ? N : RP;
+            hipLaunchKernelGGL(k_digit_hist, tiles, dim3(kBlock), 0, s, kin, in_stride, N, K,
+                               (int)first, sp.nvalid, 8 * q, sp.table, T);
+            hipLaunchKernelGGL(k_digit_colscan, dim3((unsigned)B), dim3(kDigits * kDigitGroups),
+                               0, s, sp.table, sp.nvalid, T);
+            hipLaunchKernelGGL(k_digit_scatter, tiles, dim3(kBlock), 0, s, kin, vin, in_stride, N,
+                               K, (int)first, sp.nvalid, 8 * q, sp.table, T, kout, vout,
+                               out_stride, sp.counts, last ? sp.sums : nullptr, sp.arrive, sp.d);
+        }
     }
     return hipGetLastError();
 }

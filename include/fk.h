@@ -77,11 +77,10 @@ typedef enum fk_status {
  * Problem flags (fk_problem.flags, bitwise or; other bits must be 0).
  *
  * FK_DETERMINISTIC -- results of fk_update and fk_lloyd do not depend on
- *   timing: the same inputs give the same bits on every run.  The argsort is
- *   then stable, and segments longer than 256 points store each piece's
+ *   timing: the same inputs give the same bits on every run.  (The argsort
+ *   is always stable.)  Segments longer than 256 points store each piece's
  *   partial sums (workspace) and add them in piece order in a second pass
- *   instead of with atomics.  Needs K <= 16000 (the tiled argsort; larger K
- *   gives FK_EUNSUPPORTED) and is not available for fk_lloyd_streamed.  The
+ *   instead of with atomics.  Not available for fk_lloyd_streamed.  The
  *   workspace grows by B * (ceil(N/256) + K) * d * 4 bytes.
  */
 #define FK_DETERMINISTIC 1
@@ -152,8 +151,8 @@ fk_status fk_assign_with_bias(const fk_problem* p, const void* X, const void* C,
  *                       number of labels in [0, K), N when all are valid);
  *   sorted_idx [B][N]   point indices grouped by label: positions
  *                       offsets[b][k] .. offsets[b][k+1]-1 hold the points of
- *                       label k, in increasing index order for K <= 16000
- *                       (a stable argsort), in unspecified order otherwise.
+ *                       label k, in increasing index order (a stable
+ *                       argsort).
  * Labels outside [0, K) are skipped and counted (fk_error_count).
  */
 fk_status fk_sort_labels(const fk_problem* p, const int32_t* labels, int32_t* counts,
@@ -174,11 +173,11 @@ fk_status fk_sort_labels(const fk_problem* p, const int32_t* labels, int32_t* co
  *     may be NULL (must be NULL or distinct from C_next for fp32);
  *   counts [B][K] int32.
  * The fp32 sums follow the sorted order within each segment (increasing
- * point index for K <= 16000) and, for segments longer than 256 points, the
- * order of the atomic additions of their pieces, so without FK_DETERMINISTIC
- * the low bits of such centroids (and of every centroid for K > 16000) can
- * differ between runs; with it they cannot.  Counts never differ.  Labels
- * outside [0, K) are skipped and counted (fk_error_count).
+ * point index) and, for segments longer than 256 points, the order of the
+ * atomic additions of their pieces, so without FK_DETERMINISTIC the low
+ * bits of such centroids can differ between runs; with it they cannot.
+ * Counts never differ.  Labels outside [0, K) are skipped and counted
+ * (fk_error_count).
  */
 fk_status fk_update(const fk_problem* p, const void* X, const int32_t* labels,
                     const float* C_prev, float* C_next, void* C_next_lowp, int32_t* counts,

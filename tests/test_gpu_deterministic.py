@@ -18,8 +18,10 @@ def gpu():
     assert torch.cuda.is_available(), "GPU tests need an MI355X"
 
 
-@pytest.mark.parametrize("K", [1, 7, 1000, 4096, 16000])
+@pytest.mark.parametrize("K", [1, 7, 1000, 4096, 16000, 16001, 65536, 70000])
 def test_argsort_is_stable(K):
+    """Tiled counting sort up to K = 16000, radix passes above (two for
+    K <= 65536, three beyond)."""
     B, N = 2, 3 * 4096 + 1234          # several sort tiles and a ragged tail
     rng = np.random.Generator(np.random.PCG64(K))
     lab = rng.integers(0, K, size=(B, N)).astype(np.int32)
@@ -111,10 +113,10 @@ def test_deterministic_api():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-def test_deterministic_needs_tiled_sort():
-    X = torch.randn((1, 100, 8)).half().cuda()
-    labels = torch.zeros((1, 100), dtype=torch.int32, device="cuda")
-    C = torch.zeros((1, 20000, 8), device="cuda")
-    counts = torch.empty((1, 20000), dtype=torch.int32, device="cuda")
-    with pytest.raises(fk.FKError):
-        fk.fk_update(X, labels, C, C, None, counts, deterministic=True)
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_deterministic_update_large_K(dt):
+    """K above the tiled sort (radix argsort), long and empty segments."""
+    X, C, labels = skewed_case(2, 30000, 20000, 64, dt, seed=7)
+    runs = [run_update(X, C, labels, True) for _ in range(2)]
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][2], runs[1][2])
+    check_update(X, labels, C, runs[0][0], runs[0][2], C_lowp=runs[0][1])
