@@ -192,10 +192,11 @@ def fk_lloyd(X: torch.Tensor, C: torch.Tensor, labels: torch.Tensor, counts: tor
 
 def fk_lloyd_streamed(X_host: torch.Tensor, C: torch.Tensor, labels: torch.Tensor,
                       counts: torch.Tensor, max_iters: int, chunk_points: int,
-                      ws: torch.Tensor | None = None, compute_stream=None, copy_stream=None) -> None:
+                      ws: torch.Tensor | None = None, compute_stream=None, copy_stream=None,
+                      deterministic: bool = False) -> None:
     """Lloyd iterations on a pinned host tensor X_host (B, N, d), streamed to
     the GPU in chunks of chunk_points points; C, labels, counts on the GPU."""
-    p = _problem_from(X_host, C.shape[1])
+    p = _problem_from(X_host, C.shape[1], deterministic)
     if not X_host.is_pinned():
         raise ValueError("X_host must be a pinned CPU tensor (pin_memory=True)")
     ws = workspace(p, C.device, chunk_points) if ws is None else ws

@@ -100,6 +100,11 @@ StreamWorkspace stream_workspace_layout(const fk_problem& p, int64_t chunk, char
         take((1 + 2 * (size_t)piece_capacity(chunk, p.K)) * sizeof(int32_t)));
     w.part = reinterpret_cast<int32_t*>(take(2 * (size_t)plan_blocks(p.K) * sizeof(int32_t)));
     w.bad = reinterpret_cast<int32_t*>(take(256));
+    if (p.flags & FK_DETERMINISTIC) {
+        w.csums = reinterpret_cast<float*>(take(K * d * sizeof(float)));
+        w.psums = reinterpret_cast<float*>(
+            take((size_t)piece_capacity(chunk, p.K) * d * sizeof(float)));
+    }
     w.total = o;
     return w;
 }
@@ -232,8 +237,6 @@ fk_status fk_workspace_size(const fk_problem* p, int64_t chunk_points, size_t* b
     if (!bytes) return fail(FK_EINVAL, "bytes is NULL");
     if (chunk_points < 0) return fail(FK_EINVAL, "chunk_points must be >= 0");
     if (chunk_points > kMaxIndex) return fail(FK_EUNSUPPORTED, "chunk_points too large");
-    if (chunk_points > 0 && (p->flags & FK_DETERMINISTIC))
-        return fail(FK_EUNSUPPORTED, "FK_DETERMINISTIC is not available for the streamed path");
     *bytes = chunk_points == 0
                  ? workspace_layout(*p, nullptr).total
                  : stream_workspace_layout(*p, chunk_points < p->N ? chunk_points : p->N, nullptr).total;
@@ -384,8 +387,6 @@ fk_status fk_lloyd_streamed(const fk_problem* p, const void* X_host, int64_t chu
     FK_CHECK(check_ptr(counts, "counts"));
     if (chunk_points < 1) return fail(FK_EINVAL, "chunk_points must be >= 1");
     if (chunk_points > kMaxIndex) return fail(FK_EUNSUPPORTED, "chunk_points too large");
-    if (p->flags & FK_DETERMINISTIC)
-        return fail(FK_EUNSUPPORTED, "FK_DETERMINISTIC is not available for the streamed path");
     if (max_iters < 1) return fail(FK_EINVAL, "max_iters must be >= 1");
     if (p->d > 1024) return fail(FK_EUNSUPPORTED, "update supports d <= 1024");
     const int64_t chunk = chunk_points < p->N ? chunk_points : p->N;
@@ -460,11 +461,23 @@ fk_status fk_lloyd_streamed(const fk_problem* p, const void* X_host, int64_t chu
                     so.nvalid = w.nvalid;
                     so.bad = w.bad;
                     FK_TRY(launch_sort(so, 1, n, K, cs), "sort chunk labels");
-                    const SegParams sp{false, w.sums + b * K * d, nullptr, nullptr, nullptr,
-                                       nullptr, nullptr, nullptr};
-                    FK_TRY(launch_segment_sums(dt, w.xbuf[buf], w.sorted_idx, w.offsets, w.pieces,
-                                               sp, 1, n, K, (int)d, cs),
-                           "segment sums");
+                    if (w.csums) {
+                        // deterministic: this chunk's sums stored (pieces merged in
+                        // order), then added to the running sums in chunk order
+                        const SegParams sp{true, w.csums, nullptr, nullptr, nullptr, nullptr,
+                                           nullptr, nullptr, w.psums, w.poff};
+                        FK_TRY(launch_segment_sums(dt, w.xbuf[buf], w.sorted_idx, w.offsets,
+                                                   w.pieces, sp, 1, n, K, (int)d, cs),
+                               "segment sums");
+                        FK_TRY(launch_add_f32(w.sums + b * K * d, w.csums, K * d, cs),
+                               "add chunk sums");
+                    } else {
+                        const SegParams sp{false, w.sums + b * K * d, nullptr, nullptr, nullptr,
+                                           nullptr, nullptr, nullptr};
+                        FK_TRY(launch_segment_sums(dt, w.xbuf[buf], w.sorted_idx, w.offsets,
+                                                   w.pieces, sp, 1, n, K, (int)d, cs),
+                               "segment sums");
+                    }
                     FK_TRY(launch_add_i32(counts + b * K, w.ccounts, K, cs), "add counts");
                     FK_TRY(hipEventRecord(done[buf], cs), "record done");
                 }

@@ -82,6 +82,8 @@ struct StreamWorkspace {
     int32_t* pieces;     // [1 + 2 * piece_capacity(chunk)]
     int32_t* part;       // [2 * plan_blocks(K)]
     int32_t* bad;        // [1]
+    float* csums;        // [K][d] one chunk's segment sums (FK_DETERMINISTIC), or null
+    float* psums;        // [piece_capacity(chunk)][d] piece partials (FK_DETERMINISTIC), or null
     size_t total;
 };
 
@@ -107,7 +109,9 @@ struct SortParams {
 };
 
 // Argument block of the segment sums.  final: fused finalize into C_next
-// (sums and arrive must be zero); otherwise partial sums are added to sums.
+// (sums and arrive must be zero), or, with C_next null, every segment's sum
+// row stored into sums (sums mode, zero rows for empty segments); otherwise
+// partial sums are added to sums.
 struct SegParams {
     bool final;
     float* sums;
@@ -131,6 +135,7 @@ hipError_t launch_fill_u32(uint32_t* ptr, int64_t n, uint32_t value, hipStream_t
 
 // dst[i] += src[i]
 hipError_t launch_add_i32(int32_t* dst, const int32_t* src, int64_t n, hipStream_t s);
+hipError_t launch_add_f32(float* dst, const float* src, int64_t n, hipStream_t s);
 
 hipError_t launch_centroid_bias(int dtype, const void* C, float* bias, int64_t rows, int d,
                                 hipStream_t s);

@@ -63,6 +63,12 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
         p[i] = v;
 }
 
+__global__ void k_add_f32(float* __restrict__ dst, const float* __restrict__ src, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        dst[i] += src[i];
+}
+
 __global__ void k_add_i32(int32_t* __restrict__ dst, const int32_t* __restrict__ src, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x)
@@ -735,6 +741,13 @@ template <typename T, int EPL, bool VEC>
 __device__ inline void finalize_row(const SegOut<T>& o, int64_t b, int64_t K, int d, int64_t k,
                                     int32_t count, const float (&s)[EPL], int e0) {
     const int64_t base = (b * K + k) * d;
+    if (!o.C_next) {
+        // sums mode: the segment's sum row itself
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            if (e0 + e < d) o.sums[base + e0 + e] = s[e];
+        return;
+    }
     const float fn = (float)count;
     float cn = 0.f, mv = 0.f;
 #pragma unroll
@@ -797,6 +810,10 @@ __global__ __launch_bounds__(kBlock) void k_segment_sums(
             const int64_t k = ((int64_t)blockIdx.x - piece_wgs) * (kBlock / kWave) + wave;
             if (k >= K || off[k + 1] != off[k]) return;
             const int64_t base = (b * K + k) * d;
+            if (!o.C_next) {  // sums mode: an empty segment sums to zero
+                for (int j = lane; j < d; j += kWave) o.sums[base + j] = 0.f;
+                return;
+            }
             float cn = 0.f;
             for (int j = lane; j < d; j += kWave) {
                 const float c = o.C_prev[base + j];
@@ -947,6 +964,10 @@ __global__ __launch_bounds__(kBlock) void k_merge_pieces(const int32_t* __restri
     for (int j = lane; j < d; j += kWave) {
         float sum = 0.f;
         for (int32_t q = 0; q < np; ++q) sum += ps[(int64_t)q * d + j];
+        if (!o.C_next) {  // sums mode
+            o.sums[base + j] = sum;
+            continue;
+        }
         const float c = sum / fn;
         const float prev = o.C_prev[base + j];
         o.C_next[base + j] = c;
@@ -960,6 +981,7 @@ __global__ __launch_bounds__(kBlock) void k_merge_pieces(const int32_t* __restri
         const float m = c - prev;
         mv = fmaf(m, m, mv);
     }
+    if (!o.C_next) return;
     if (o.bias) {
         cn = wave_sum(cn);
         if (lane == 0) o.bias[b * K + k] = -0.5f * cn;
@@ -1092,6 +1114,13 @@ hipError_t launch_fill_u32(uint32_t* ptr, int64_t n, uint32_t value, hipStream_t
     if (n <= 0) return hipSuccess;
     const int64_t blocks = min((n + kBlock - 1) / kBlock, (int64_t)4096);
     hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(kBlock), 0, s, ptr, n, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_add_f32(float* dst, const float* src, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = min((n + kBlock - 1) / kBlock, (int64_t)4096);
+    hipLaunchKernelGGL(k_add_f32, dim3((unsigned)blocks), dim3(kBlock), 0, s, dst, src, n);
     return hipGetLastError();
 }
 

@@ -80,8 +80,10 @@ typedef enum fk_status {
  *   timing: the same inputs give the same bits on every run.  (The argsort
  *   is always stable.)  Segments longer than 256 points store each piece's
  *   partial sums (workspace) and add them in piece order in a second pass
- *   instead of with atomics.  Not available for fk_lloyd_streamed.  The
- *   workspace grows by B * (ceil(N/256) + K) * d * 4 bytes.
+ *   instead of with atomics; fk_lloyd_streamed stores each chunk's sums and
+ *   adds them to the running sums in chunk order.  The workspace grows by
+ *   B * (ceil(N/256) + K) * d * 4 bytes (streamed: (ceil(chunk/256) + 2 K)
+ *   * d * 4 bytes).
  */
 #define FK_DETERMINISTIC 1
 

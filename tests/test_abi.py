@@ -75,12 +75,12 @@ def test_unknown_dtype_rejected():
     assert call_assign(P(dtype=7), ws_bytes=1 << 30) == fk.FK_EUNSUPPORTED
 
 
-def test_deterministic_streamed_rejected():
+def test_deterministic_workspace_is_larger():
     p = P(flags=fk.FK_DETERMINISTIC)
     n = ctypes.c_size_t(0)
-    assert fk.lib.fk_workspace_size(ctypes.byref(p), 0, ctypes.byref(n)) == fk.FK_OK
-    assert n.value > fk.workspace_size(P())
-    assert fk.lib.fk_workspace_size(ctypes.byref(p), 64, ctypes.byref(n)) == fk.FK_EUNSUPPORTED
+    for chunk in (0, 64):
+        assert fk.lib.fk_workspace_size(ctypes.byref(p), chunk, ctypes.byref(n)) == fk.FK_OK
+        assert n.value > fk.workspace_size(P(), chunk)
 
 
 def test_unknown_flags_rejected():

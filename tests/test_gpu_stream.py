@@ -51,6 +51,27 @@ def test_streamed_lockstep(cfg, kw, chunk, iters):
         check_update(Xg, labels, C_prev, C, counts)
 
 
+def test_streamed_deterministic():
+    """FK_DETERMINISTIC on the streamed path: bit-identical reruns, and one
+    iteration still matches the oracle (Zipf sizes: long segments)."""
+    X, C0 = synth.make(3, N=40000, K=128)
+    Xh = pinned(X)
+    outs = []
+    for _ in range(2):
+        C = C0.cuda().clone()
+        labels = torch.empty((1, 40000), dtype=torch.int32, device="cuda")
+        counts = torch.empty((1, 128), dtype=torch.int32, device="cuda")
+        fk.fk_lloyd_streamed(Xh, C, labels, counts, 1, 9000, copy_stream=torch.cuda.Stream(),
+                             deterministic=True)
+        torch.cuda.synchronize()
+        outs.append((C, labels, counts))
+    assert int(outs[0][2].max()) > 256
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    Xg = X.cuda()
+    check_labels(outs[0][1], Xg, C0.cuda().to(X.dtype))
+    check_update(Xg, outs[0][1], C0.cuda(), outs[0][0], outs[0][2])
+
+
 def test_streamed_matches_resident():
     X, C0 = synth.make(1)
     Xh = pinned(X)
