@@ -48,8 +48,9 @@ struct Mfma16<__bf16> {
 //
 // Tile of 32 centroids = 2 row blocks of 16.  A slot is the NP MFMAs that
 // share one centroid fragment (row block rb, k-step s), slot order s-major;
-// each slot is preceded by the epilogue of one row (rb, i) of tile t for all
-// NP point blocks.  Staging (registers -> ring of four LDS buffers), the
+// in each slot every MFMA is followed by the epilogue of one row of tile t
+// for its point block (rows spread evenly over the slots).  Staging
+// (registers -> ring of four LDS buffers), the
 // prefetch of the next tile's fragments and bias, and the branch-free
 // overlapping last tile are those of k_assign.
 template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK, bool MAT, int W>
@@ -183,16 +184,18 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
                 rt[np] = -1;
             }
         };
-        // row r = 4 rb + i of all point blocks
-        auto epi_row = [&](const floatx4 (&sc)[RB][NP], int r) {
+        // row r = 4 rb + i of point block np
+        auto epi_one = [&](const floatx4 (&sc)[RB][NP], int r, int np) {
             const int rb = r >> 2, i = r & 3;
+            const float s = sc[rb][np][i];
+            const bool keep = !(s > m[np]);
+            m[np] = keep ? m[np] : s;
+            rt[np] = keep ? rt[np] : 16 * rb + i;
+        };
+        // row r of all point blocks
+        auto epi_row = [&](const floatx4 (&sc)[RB][NP], int r) {
 #pragma unroll
-            for (int np = 0; np < NP; ++np) {
-                const float s = sc[rb][np][i];
-                const bool keep = !(s > m[np]);
-                m[np] = keep ? m[np] : s;
-                rt[np] = keep ? rt[np] : 16 * rb + i;
-            }
+            for (int np = 0; np < NP; ++np) epi_one(sc, r, np);
         };
         // MAT: lane (g, col) holds scores of centroids 16 rb + 4 g + i
         // (i = 0..3) of point col of each block
@@ -271,14 +274,19 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
 #pragma unroll
             for (int sl = 0; sl < kSlots; ++sl) {
                 const int s = sl / RB, rb = sl % RB;
-                if constexpr (!MAT) {
+                // each MFMA is followed by the compares of one (row, point
+                // block) pair of the previous tile, so they issue while the
+                // matrix unit works on it
 #pragma unroll
-                    for (int r = 8 * sl / kSlots; r < 8 * (sl + 1) / kSlots; ++r) epi_row(prv, r);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int np = 0; np < NP; ++np)
+                for (int np = 0; np < NP; ++np) {
                     cur[rb][np] = M::step(a[sl], xf[np][s], s == 0 ? bv[rb] : cur[rb][np]);
+                    if constexpr (!MAT) {
+#pragma unroll
+                        for (int r = 8 * sl / kSlots; r < 8 * (sl + 1) / kSlots; ++r)
+                            epi_one(prv, r, np);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 // a[sl] is free: read the fragment needed P slots later
                 const int v = sl + P;
                 if (v < kSlots)
