@@ -22,6 +22,16 @@
 namespace fk {
 namespace {
 
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1: loop bodies whose
+// bounds depend on an outer index stay compile-time constants.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 template <typename T>
 struct Mfma16;
 
@@ -274,19 +284,39 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
 #pragma unroll
             for (int sl = 0; sl < kSlots; ++sl) {
                 const int s = sl / RB, rb = sl % RB;
-                // each MFMA is followed by the compares of one (row, point
-                // block) pair of the previous tile, so they issue while the
-                // matrix unit works on it
-#pragma unroll
-                for (int np = 0; np < NP; ++np) {
-                    cur[rb][np] = M::step(a[sl], xf[np][s], s == 0 ? bv[rb] : cur[rb][np]);
+                // The slot's rows of the previous tile's epilogue are spread
+                // over its MFMAs so they issue while the matrix unit works:
+                // per row, one group of compares for all point blocks (masks
+                // kept in SGPRs), then two groups of selects; group g follows
+                // MFMA g * NP / G.
+                bool upd[NP];
+                static_for<0, NP>([&](auto Q) {
+                    constexpr int q = decltype(Q)::value;
+                    cur[rb][q] = M::step(a[sl], xf[q][s], s == 0 ? bv[rb] : cur[rb][q]);
                     if constexpr (!MAT) {
+                        // rows r0 .. r1-1 of this slot, G groups
+                        static_for<0, 12>([&](auto GG) {
+                            constexpr int g = decltype(GG)::value;
+                            if (g >= 3 * (8 * (sl + 1) / kSlots - 8 * sl / kSlots)) return;
+                            const int G = 3 * (8 * (sl + 1) / kSlots - 8 * sl / kSlots);
+                            if (g * NP / G != q) return;
+                            const int r = 8 * sl / kSlots + g / 3, prb = r >> 2, pi = r & 3;
+                            if constexpr (g % 3 == 0) {
 #pragma unroll
-                        for (int r = 8 * sl / kSlots; r < 8 * (sl + 1) / kSlots; ++r)
-                            epi_one(prv, r, np);
+                                for (int np = 0; np < NP; ++np) upd[np] = prv[prb][np][pi] > m[np];
+                            } else {
+                                constexpr int lo = g % 3 == 1 ? 0 : NP / 2;
+                                constexpr int hi = g % 3 == 1 ? NP / 2 : NP;
+#pragma unroll
+                                for (int np = lo; np < hi; ++np) {
+                                    m[np] = upd[np] ? prv[prb][np][pi] : m[np];
+                                    rt[np] = upd[np] ? 16 * prb + pi : rt[np];
+                                }
+                            }
+                        });
                     }
                     __builtin_amdgcn_sched_barrier(0);
-                }
+                });
                 // a[sl] is free: read the fragment needed P slots later
                 const int v = sl + P;
                 if (v < kSlots)
