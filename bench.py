@@ -656,6 +656,44 @@ def summarize(argv) -> int:
                "assign_sources_sha256_16": assign_sources_hash()}
         print(json.dumps(rec, indent=1))
         return 0
+    if kind == "counters":
+        # SQ counters of the assign dispatches from several --pmc passes:
+        # per-SIMD busy fractions against the GRBM clock count (summed over
+        # the 8 XCDs, so divided by 8) of the same dispatches
+        paths, cmd = [a for a in argv[1:] if a.endswith(".csv")], \
+            " ".join(a for a in argv[1:] if not a.endswith(".csv"))
+        agg, grbm, dur = {}, [], []
+        for path in paths:
+            for r in csv.DictReader(open(path)):
+                if "k_assign" not in r["Kernel_Name"]:
+                    continue
+                name = r["Counter_Name"]
+                v = float(r["Counter_Value"])
+                if name == "GRBM_GUI_ACTIVE":
+                    grbm.append(v / 8)
+                    dur.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                else:
+                    agg.setdefault(name, []).append(v)
+        cyc = sum(grbm) / len(grbm)
+        mean = {k: sum(v) / len(v) for k, v in agg.items()}
+        simds = 1024
+        print(f"# SQ counters of the assign kernel\n\ncommand: `{cmd}`\n")
+        print(f"- dispatches per pass: {len(grbm) // max(1, len(paths))}; clock "
+              f"{cyc / (sum(dur) / len(dur)):.3f} GHz (GRBM_GUI_ACTIVE per XCD / duration)")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            print(f"- matrix unit busy: {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / simds / cyc:.3f} "
+                  "of the cycles per SIMD (SQ_VALU_MFMA_BUSY_CYCLES)")
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in mean:
+            print(f"- matrix and vector units together: "
+                  f"{mean['SQ_VALU_MFMA_COEXEC_CYCLES'] / simds / cyc:.3f} (SQ_VALU_MFMA_COEXEC_CYCLES)")
+        if "SQ_INSTS_VALU" in mean and "SQ_INSTS_MFMA" in mean:
+            valu = mean["SQ_INSTS_VALU"] - mean["SQ_INSTS_MFMA"]
+            print(f"- vector unit busy: {4 * valu / simds / cyc:.3f} (SQ_INSTS_VALU minus "
+                  "SQ_INSTS_MFMA, 4 cycles per wave64 instruction)")
+        print("\n| counter | mean per dispatch |\n|---|---|")
+        for k in sorted(mean):
+            print(f"| {k} | {mean[k]:.0f} |")
+        return 0
     log(f"unknown summary kind {kind!r}")
     return 2
 
