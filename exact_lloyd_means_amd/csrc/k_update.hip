@@ -459,6 +459,88 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(
     }
 }
 
+// The same scatter for K <= kWaveBinsMax without barriers between the
+// waves: wave w takes the 1024 consecutive elements i0 + 1024 w + [0, 1024)
+// in 16 rounds of 64.  A first pass counts each wave's labels (the 16-bit
+// counts of two waves share a 32-bit LDS word), the counts become per-wave
+// exclusive prefixes, and a second pass ranks each round's lanes by ballot
+// match and advances the wave's own 16-bit cursor with one LDS atomic per
+// label group; the waves' ranges and the rounds inside a wave are in index
+// order, so the scatter is stable.
+constexpr int64_t kWaveBinsMax = 4096;
+constexpr int kWaveRange = kSortTile / (kBlock / kWave);  // elements per wave
+__global__ __launch_bounds__(kBlock) void k_tile_scatter_w(
+    const int32_t* __restrict__ labels, const int32_t* __restrict__ th,
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_idx,
+    const int32_t* __restrict__ counts, float* __restrict__ sums, int32_t* __restrict__ arrive,
+    int64_t N, int64_t K, int64_t T, int64_t d, int xcd_map, int nbits) {
+    extern __shared__ int32_t s_mem[];  // base [K] | cursors of waves 0,1 [K] | of waves 2,3 [K]
+    int32_t* s_base = s_mem;
+    uint32_t* s_cur = reinterpret_cast<uint32_t*>(s_mem + K);
+    int64_t b, t;
+    if (xcd_map) {
+        const int64_t x = blockIdx.x % 8, q = blockIdx.x / 8;
+        b = x + 8 * (q / T);
+        t = q % T;
+    } else {
+        b = blockIdx.y;
+        t = blockIdx.x;
+    }
+    if (sums) clear_multi_rows(counts + b * K, sums + b * K * d, arrive + b * K, K, d, t, T);
+    const int32_t* pre = th + (b * T + t) * (K + 1);
+    const int32_t* off = offsets + b * (K + 1);
+    for (int64_t k = threadIdx.x; k < K; k += kBlock) {
+        s_base[k] = off[k] + pre[k];
+        s_cur[k] = 0u;
+        s_cur[K + k] = 0u;
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t w0 = t * kSortTile + (int64_t)wave * kWaveRange;
+    const int64_t i1 = min(t * kSortTile + (int64_t)kSortTile, N);
+    const int32_t* lab = labels + b * N;
+    int32_t* out = sorted_idx + b * N;
+    uint32_t* cur = s_cur + (wave >> 1) * K;
+    const uint32_t sh = 16u * (uint32_t)(wave & 1);
+    int32_t a[kSortPer];
+#pragma unroll
+    for (int j = 0; j < kSortPer; ++j) {
+        const int64_t i = w0 + j * kWave + lane;
+        a[j] = i < i1 ? lab[i] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kSortPer; ++j)
+        if (a[j] >= 0 && a[j] < K) atomicAdd(&cur[a[j]], 1u << sh);
+    __syncthreads();
+    for (int64_t k = threadIdx.x; k < K; k += kBlock) {
+        const uint32_t c01 = s_cur[k], c23 = s_cur[K + k];
+        const uint32_t p1 = c01 & 0xffffu, p2 = p1 + (c01 >> 16), p3 = p2 + (c23 & 0xffffu);
+        s_cur[k] = p1 << 16;
+        s_cur[K + k] = p2 | (p3 << 16);
+    }
+    __syncthreads();
+    const uint64_t below = lane ? ~0ull >> (64 - lane) : 0ull;
+#pragma unroll
+    for (int j = 0; j < kSortPer; ++j) {
+        const int64_t i = w0 + j * kWave + lane;
+        const int32_t v = a[j];
+        const bool valid = v >= 0 && v < K;
+        uint64_t peers = __ballot(valid);
+        for (int bit = 0; bit < nbits; ++bit) {
+            const bool on = (v >> bit) & 1;
+            const uint64_t m = __ballot(on);
+            peers &= on ? m : ~m;
+        }
+        if (!valid) peers = 0;
+        const int rank = __popcll(peers & below);
+        uint32_t old = 0;
+        if (valid && rank == 0) old = atomicAdd(&cur[v], (uint32_t)__popcll(peers) << sh);
+        old = __shfl(old, valid ? __ffsll((unsigned long long)peers) - 1 : lane);
+        if (valid) out[s_base[v] + (int32_t)((old >> sh) & 0xffffu) + rank] = (int32_t)i;
+    }
+}
+
 // ---- counting sort with global atomics (large K) ----------------------------
 // counts[b][k] += #{i in tile : labels[b][i] == k}; labels out of [0, K) are
 // counted in bad[b] and skipped.
@@ -1198,9 +1280,15 @@ hipError_t launch_sort(const SortParams& sp, int64_t B, int64_t N, int64_t K, hi
         const int xcd_map = B % 8 == 0 && T * B < ((int64_t)1 << 31);
         const dim3 sgrid = xcd_map ? dim3((unsigned)(T * B)) : tiles;
         const int nbits = K > 1 ? 64 - __builtin_clzll((unsigned long long)(K - 1)) : 0;
-        hipLaunchKernelGGL(k_tile_scatter, sgrid, dim3(kBlock), (size_t)K * sizeof(int32_t), s,
-                           sp.labels, sp.table, sp.offsets, sp.sorted_idx, sp.counts, sp.sums,
-                           sp.arrive, N, K, T, sp.d, xcd_map, nbits);
+        if (K <= kWaveBinsMax)
+            hipLaunchKernelGGL(k_tile_scatter_w, sgrid, dim3(kBlock),
+                               (size_t)(3 * K) * sizeof(int32_t), s, sp.labels, sp.table,
+                               sp.offsets, sp.sorted_idx, sp.counts, sp.sums, sp.arrive, N, K, T,
+                               sp.d, xcd_map, nbits);
+        else
+            hipLaunchKernelGGL(k_tile_scatter, sgrid, dim3(kBlock), (size_t)K * sizeof(int32_t), s,
+                               sp.labels, sp.table, sp.offsets, sp.sorted_idx, sp.counts, sp.sums,
+                               sp.arrive, N, K, T, sp.d, xcd_map, nbits);
     } else {
         // LSD radix passes over 8-bit digits; pairs ping-pong between the
         // two halves of the radix buffer, the last pass writes sorted_idx
