@@ -684,9 +684,10 @@ __global__ __launch_bounds__(kDigits * kDigitGroups) void k_digit_colscan(
 
 // Stable scatter of one pass: element i of tile t goes to
 // dth[b][t][digit] + (its rank among the tile's elements of that digit, in
-// index order), ranked as in k_tile_scatter (ballots over the 8 digit bits,
-// then wave by wave).  keys_out may be null (last pass: values only).  With
-// sums the workgroups also clear the sum rows of multi-piece segments.
+// index order), with wave-private cursors as in k_tile_scatter_w (wave w
+// takes 1024 consecutive elements; two waves' 16-bit counts share a word).
+// keys_out may be null (last pass: values only).  With sums the workgroups
+// also clear the sum rows of multi-piece segments.
 __global__ __launch_bounds__(kBlock) void k_digit_scatter(
     const int32_t* __restrict__ keys, const int32_t* __restrict__ vals, int64_t in_stride,
     int64_t N, int64_t K, int first, const int32_t* __restrict__ nvalid, int shift,
@@ -694,31 +695,46 @@ __global__ __launch_bounds__(kBlock) void k_digit_scatter(
     int32_t* __restrict__ vals_out, int64_t out_stride, const int32_t* __restrict__ counts,
     float* __restrict__ sums, int32_t* __restrict__ arrive, int64_t d) {
     __shared__ int32_t s_base[kDigits];
+    __shared__ uint32_t s_cur[2][kDigits];
     const int64_t b = blockIdx.y, t = blockIdx.x;
     if (sums) clear_multi_rows(counts + b * K, sums + b * K * d, arrive + b * K, K, d, t, T);
     s_base[threadIdx.x] = dth[(b * T + t) * kDigits + threadIdx.x];
+    s_cur[0][threadIdx.x] = 0u;
+    s_cur[1][threadIdx.x] = 0u;
     __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int64_t n = first ? N : nvalid[b];
-    const int64_t i0 = t * kSortTile;
-    const int64_t i1 = min(i0 + (int64_t)kSortTile, n);
+    const int64_t w0 = t * kSortTile + (int64_t)wave * kWaveRange;
+    const int64_t i1 = min(t * kSortTile + (int64_t)kSortTile, n);
     const int32_t* kin = keys + b * in_stride;
     const int32_t* vin = vals ? vals + b * in_stride : nullptr;
     int32_t* kout = keys_out ? keys_out + b * out_stride : nullptr;
     int32_t* vout = vals_out + b * out_stride;
+    uint32_t* cur = s_cur[wave >> 1];
+    const uint32_t sh = 16u * (uint32_t)(wave & 1);
     int32_t a[kSortPer], v[kSortPer];
 #pragma unroll
     for (int j = 0; j < kSortPer; ++j) {
-        const int64_t i = i0 + threadIdx.x + j * kBlock;
+        const int64_t i = w0 + j * kWave + lane;
         a[j] = i < i1 ? kin[i] : -1;
         v[j] = vin ? (i < i1 ? vin[i] : 0) : (int32_t)i;
     }
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < kSortPer; ++j)
+        if (a[j] >= 0 && a[j] < K) atomicAdd(&cur[(a[j] >> shift) & (kDigits - 1)], 1u << sh);
+    __syncthreads();
+    {
+        const uint32_t c01 = s_cur[0][threadIdx.x], c23 = s_cur[1][threadIdx.x];
+        const uint32_t p1 = c01 & 0xffffu, p2 = p1 + (c01 >> 16), p3 = p2 + (c23 & 0xffffu);
+        s_cur[0][threadIdx.x] = p1 << 16;
+        s_cur[1][threadIdx.x] = p2 | (p3 << 16);
+    }
+    __syncthreads();
     const uint64_t below = lane ? ~0ull >> (64 - lane) : 0ull;
 #pragma unroll
     for (int j = 0; j < kSortPer; ++j) {
-        const int64_t i = i0 + threadIdx.x + j * kBlock;
-        const bool valid = i < i1 && a[j] >= 0 && a[j] < K;
+        const bool valid = a[j] >= 0 && a[j] < K;
         const int32_t dig = (a[j] >> shift) & (kDigits - 1);
         uint64_t peers = __ballot(valid);
 #pragma unroll
@@ -729,14 +745,11 @@ __global__ __launch_bounds__(kBlock) void k_digit_scatter(
         }
         if (!valid) peers = 0;
         const int rank = __popcll(peers & below);
-        int32_t base = 0;
-        for (int w = 0; w < kBlock / kWave; ++w) {
-            if (wave == w && valid && rank == 0) base = atomicAdd(&s_base[dig], __popcll(peers));
-            __syncthreads();
-        }
-        base = __shfl(base, valid ? __ffsll((unsigned long long)peers) - 1 : lane);
+        uint32_t old = 0;
+        if (valid && rank == 0) old = atomicAdd(&cur[dig], (uint32_t)__popcll(peers) << sh);
+        old = __shfl(old, valid ? __ffsll((unsigned long long)peers) - 1 : lane);
         if (valid) {
-            const int32_t pos = base + rank;
+            const int32_t pos = s_base[dig] + (int32_t)((old >> sh) & 0xffffu) + rank;
             if (kout) kout[pos] = a[j];
             vout[pos] = v[j];
         }
