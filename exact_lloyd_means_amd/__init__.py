@@ -48,6 +48,7 @@ _SIG = {
     "fk_assign_with_bias": ([_PP, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "fk_sort_labels": ([_PP, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "fk_update": ([_PP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "fk_update_bias": ([_PP, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "fk_lloyd": ([_PP, _P, _P, _P, _P, ctypes.c_int, ctypes.c_float,
                   ctypes.POINTER(ctypes.c_int), _P, ctypes.c_size_t, _P], ctypes.c_int),
     "fk_lloyd_streamed": ([_PP, _P, ctypes.c_int64, _P, _P, _P, ctypes.c_int, _P, ctypes.c_size_t,
@@ -174,6 +175,18 @@ def fk_update(X: torch.Tensor, labels: torch.Tensor, C_prev: torch.Tensor, C_nex
     _check(lib.fk_update(ctypes.byref(p), _ptr(X), _ptr(labels), _ptr(C_prev), _ptr(C_next),
                          _ptr(C_next_lowp), _ptr(counts), _ptr(ws), ws.numel(),
                          _stream(stream)), "fk_update")
+
+
+def fk_update_bias(X: torch.Tensor, labels: torch.Tensor, C_prev: torch.Tensor,
+                   C_next: torch.Tensor, C_next_lowp: torch.Tensor | None, counts: torch.Tensor,
+                   bias_next: torch.Tensor, ws: torch.Tensor | None = None, stream=None,
+                   deterministic: bool = False) -> None:
+    """fk_update that also writes the next assignment's centroid bias."""
+    p = _problem_from(X, C_prev.shape[1], deterministic)
+    ws = workspace(p, X.device) if ws is None else ws
+    _check(lib.fk_update_bias(ctypes.byref(p), _ptr(X), _ptr(labels), _ptr(C_prev), _ptr(C_next),
+                              _ptr(C_next_lowp), _ptr(counts), _ptr(bias_next), _ptr(ws),
+                              ws.numel(), _stream(stream)), "fk_update_bias")
 
 
 def fk_lloyd(X: torch.Tensor, C: torch.Tensor, labels: torch.Tensor, counts: torch.Tensor,

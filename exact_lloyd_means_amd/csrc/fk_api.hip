@@ -299,9 +299,12 @@ fk_status fk_sort_labels(const fk_problem* p, const int32_t* labels, int32_t* co
     return enqueue_sort(*p, w, labels, counts, offsets, sorted_idx, false, nullptr, s);
 }
 
-fk_status fk_update(const fk_problem* p, const void* X, const int32_t* labels,
-                    const float* C_prev, float* C_next, void* C_next_lowp, int32_t* counts,
-                    void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+fk_status update_impl(const fk_problem* p, const void* X, const int32_t* labels,
+                      const float* C_prev, float* C_next, void* C_next_lowp, int32_t* counts,
+                      float* bias_next, void* ws, size_t ws_bytes, void* stream) {
     FK_CHECK(check_problem(p));
     FK_CHECK(check_ptr(X, "X"));
     FK_CHECK(check_ptr(labels, "labels"));
@@ -319,7 +322,7 @@ fk_status fk_update(const fk_problem* p, const void* X, const int32_t* labels,
     const int64_t rows = p->B * p->K;
     FK_CHECK(enqueue_sort(*p, w, labels, counts, w.offsets, w.sorted_idx, true, nullptr, s));
     SegParams sp{true,    w.sums,  w.arrive, C_prev, C_next,
-                 p->dtype == FK_F32 ? nullptr : C_next_lowp, nullptr, nullptr, w.psums, w.poff};
+                 p->dtype == FK_F32 ? nullptr : C_next_lowp, bias_next, nullptr, w.psums, w.poff};
     FK_TRY(launch_segment_sums(p->dtype, X, w.sorted_idx, w.offsets, w.pieces, sp, p->B, p->N,
                                p->K, (int)p->d, s),
            "segment sums");
@@ -328,6 +331,25 @@ fk_status fk_update(const fk_problem* p, const void* X, const int32_t* labels,
                               hipMemcpyDeviceToDevice, s),
                "copy fp32 centroids");
     return FK_OK;
+}
+}  // namespace
+
+extern "C" {
+
+fk_status fk_update(const fk_problem* p, const void* X, const int32_t* labels,
+                    const float* C_prev, float* C_next, void* C_next_lowp, int32_t* counts,
+                    void* ws, size_t ws_bytes, void* stream) {
+    return update_impl(p, X, labels, C_prev, C_next, C_next_lowp, counts, nullptr, ws, ws_bytes,
+                       stream);
+}
+
+fk_status fk_update_bias(const fk_problem* p, const void* X, const int32_t* labels,
+                         const float* C_prev, float* C_next, void* C_next_lowp, int32_t* counts,
+                         float* bias_next, void* ws, size_t ws_bytes, void* stream) {
+    FK_CHECK(check_problem(p));
+    FK_CHECK(check_ptr(bias_next, "bias_next"));
+    return update_impl(p, X, labels, C_prev, C_next, C_next_lowp, counts, bias_next, ws, ws_bytes,
+                       stream);
 }
 
 fk_status fk_lloyd(const fk_problem* p, const void* X, float* C, int32_t* labels,

@@ -56,6 +56,18 @@ __device__ inline float to_f32(T v) {
     return (float)v;
 }
 
+// Canonical order of a centroid row's squared norm: lane l adds the E
+// consecutive elements l E .. l E + E - 1 (E = the smallest power of two
+// with 64 E >= d) in order, then the wave adds the 64 partial sums by the
+// butterfly of wave_sum.  Every kernel that writes a centroid bias follows
+// it (the segment sums hold exactly these elements per lane), so the bias
+// has the same bits whichever kernel wrote it.
+__device__ inline int row_part(int d) {
+    int e = 1;
+    while (e * kWave < d) e <<= 1;
+    return e;
+}
+
 // ---------------------------------------------------------------------------
 __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -97,8 +109,11 @@ __global__ __launch_bounds__(kBlock) void k_centroid_bias(const T* __restrict__ 
     const int64_t row = (int64_t)blockIdx.x * (kBlock / kWave) + (threadIdx.x >> 6);
     if (row >= rows) return;
     const T* c = C + row * d;
+    const int E = row_part(d);
     float s = 0.f;
-    for (int j = lane; j < d; j += kWave) {
+    for (int e = 0; e < E; ++e) {
+        const int j = lane * E + e;
+        if (j >= d) break;
         const float v = to_f32(c[j]);
         s = fmaf(v, v, s);
     }
@@ -114,7 +129,10 @@ __global__ __launch_bounds__(kBlock) void k_prepare(const float* __restrict__ C,
     const int64_t row = (int64_t)blockIdx.x * (kBlock / kWave) + (threadIdx.x >> 6);
     if (row >= rows) return;
     float s = 0.f;
-    for (int j = lane; j < d; j += kWave) {
+    const int E = row_part(d);
+    for (int e = 0; e < E; ++e) {
+        const int j = lane * E + e;
+        if (j >= d) break;
         const T q = (T)C[row * d + j];
         lowp[row * d + j] = q;
         const float v = to_f32(q);
@@ -910,7 +928,10 @@ __global__ __launch_bounds__(kBlock) void k_segment_sums(
                 return;
             }
             float cn = 0.f;
-            for (int j = lane; j < d; j += kWave) {
+            const int E = row_part(d);
+            for (int e = 0; e < E; ++e) {
+                const int j = lane * E + e;
+                if (j >= d) break;
                 const float c = o.C_prev[base + j];
                 o.C_next[base + j] = c;
                 float cq = c;
@@ -1056,7 +1077,10 @@ __global__ __launch_bounds__(kBlock) void k_merge_pieces(const int32_t* __restri
     const int64_t base = (b * K + k) * d;
     const float fn = (float)count;
     float cn = 0.f, mv = 0.f;
-    for (int j = lane; j < d; j += kWave) {
+    const int E = row_part(d);
+    for (int e = 0; e < E; ++e) {
+        const int j = lane * E + e;
+        if (j >= d) break;
         float sum = 0.f;
         for (int32_t q = 0; q < np; ++q) sum += ps[(int64_t)q * d + j];
         if (!o.C_next) {  // sums mode
@@ -1105,7 +1129,10 @@ __global__ __launch_bounds__(kBlock) void k_finalize(float* __restrict__ sums,
     const int32_t n = counts[row];
     const float fn = (float)n;
     float cn = 0.f, mv = 0.f;
-    for (int j = lane; j < d; j += kWave) {
+    const int E = row_part(d);
+    for (int e = 0; e < E; ++e) {
+        const int j = lane * E + e;
+        if (j >= d) break;
         const int64_t o = row * d + j;
         const float prev = C_prev[o];
         const float c = n > 0 ? sums[o] / fn : prev;

@@ -186,6 +186,19 @@ fk_status fk_update(const fk_problem* p, const void* X, const int32_t* labels,
                     void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * fk_update_bias -- fk_update that also writes the centroid bias of the new
+ * centroids for the next assignment (the ||c||^2 term of papernotes.org
+ * notes, 关键设计 1, computed in the finalize instead of a separate pass):
+ * bias_next [B][K] fp32 = -0.5 |c|^2 of C_next_lowp (of C_next for fp32
+ * or when C_next_lowp is NULL), bit for bit what fk_centroid_bias would
+ * return for those values.  bias_next may be the buffer the assignment
+ * that produced labels read (work on one stream runs in order).
+ */
+fk_status fk_update_bias(const fk_problem* p, const void* X, const int32_t* labels,
+                         const float* C_prev, float* C_next, void* C_next_lowp, int32_t* counts,
+                         float* bias_next, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * fk_lloyd -- max_iters Lloyd iterations (papernotes.org notes, 整体框架
  * flowchart: assign, update, repeat until converged or the iteration limit).
  * C [B][K][d] fp32: initial centroids on entry, final ones on exit.  Each

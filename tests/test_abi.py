@@ -129,6 +129,9 @@ def test_update_and_lloyd_validation():
                               None) == fk.FK_EINVAL
     # error count: host pointer missing
     assert lib.fk_error_count(ctypes.byref(p), FAKE, n, None, None) == fk.FK_EINVAL
+    # update with bias: bias_next required
+    assert lib.fk_update_bias(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, n,
+                              None) == fk.FK_EINVAL
 
 
 def test_baseline_validation():

@@ -1,6 +1,7 @@
 """Full-size workloads in exactly the launch sequence the benchmark times
-(centroid bias -> fused assign with that bias -> in-place update writing the
-next low-precision centroids), checked against the fp64 oracle: labels on a
+(fused assign with the current bias -> in-place update writing the next
+low-precision centroids and their bias), checked against the fp64 oracle:
+labels on a
 seeded random sample of points (the oracle computes them one by one), counts
 and centroids of the update on every point."""
 import numpy as np
@@ -38,12 +39,12 @@ def test_full_size_lockstep(cfg):
     counts = torch.empty((B, K), dtype=torch.int32, device="cuda")
     ws = fk.workspace(fk.problem(B, N, K, d, X.dtype))
     rng = np.random.Generator(np.random.PCG64(500 + cfg))
+    fk.fk_centroid_bias(Cq, bias)
     for it in range(ITERS[cfg]):
         C_prev = C.clone()
         Cq_used = Cq.clone()
-        fk.fk_centroid_bias(Cq, bias)
         fk.fk_assign_with_bias(X, Cq, bias, labels)
-        fk.fk_update(X, labels, C, C, Cq if w.dtype != "f32" else None, counts, ws=ws)
+        fk.fk_update_bias(X, labels, C, C, Cq if w.dtype != "f32" else None, counts, bias, ws=ws)
         torch.cuda.synchronize()
         rows = rng.choice(B * N, size=SAMPLE[cfg], replace=False)
         print(f"[fullsize] {w.name} iteration {it}: checking", flush=True)
@@ -54,6 +55,11 @@ def test_full_size_lockstep(cfg):
         print(f"[fullsize] {w.name} iteration {it}: {st} {su}", flush=True)
         if w.dtype == "f32":
             Cq = C.clone()
+        # the bias written by the update is that of the centroids now in Cq
+        ref = torch.empty_like(bias)
+        fk.fk_centroid_bias(Cq, ref)
+        torch.cuda.synchronize()
+        assert torch.equal(bias, ref)
 
 
 def test_streamed_full_chunk_lockstep():

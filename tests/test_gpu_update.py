@@ -117,3 +117,35 @@ def test_update_out_of_range_labels_skipped():
     n_bad = fk.fk_error_count(p, ws)
     assert n_bad == int((lab < 0).sum() + (lab >= K).sum())
     check_update(X, lab, C_prev, C_next, counts)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("shape", [(2, 3000, 300, 128), (1, 5000, 40, 40), (2, 900, 500, 1000)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_update_bias_matches_centroid_bias(dt, shape):
+    """fk_update_bias: the same update as fk_update, and a next-assignment
+    bias bit-identical to fk_centroid_bias of the new (rounded) centroids,
+    for single-piece, multi-piece and empty segments."""
+    import synth
+    B, N, K, d = shape
+    X, _ = synth.make(2, B=B, N=N, K=K, d=d, dtype=dt)
+    X = X.cuda()
+    g = torch.Generator().manual_seed(N + d)
+    lab = torch.randint(0, K, (B, N), generator=g, dtype=torch.int32)
+    lab[:, : N // 3] = 1                  # a long segment; most labels unused when K > N
+    labels = lab.cuda()
+    C = torch.randn((B, K, d), generator=g).cuda()
+    Cn = torch.empty_like(C)
+    low = torch.empty((B, K, d), dtype=X.dtype, device="cuda") if dt != "f32" else None
+    counts = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    bias = torch.empty((B, K), dtype=torch.float32, device="cuda")
+    fk.fk_update_bias(X, labels, C, Cn, low, counts, bias)
+    Cn2 = torch.empty_like(C)
+    counts2 = torch.empty_like(counts)
+    fk.fk_update(X, labels, C, Cn2, None, counts2)
+    ref = torch.empty_like(bias)
+    fk.fk_centroid_bias(low if low is not None else Cn, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(counts, counts2)
+    assert torch.equal(bias, ref)
+    check_update(X, labels, C, Cn, counts, C_lowp=low)
