@@ -9,6 +9,8 @@
 #include "../../include/fk_baseline.h"
 #include "../../include/fk_tune.h"
 
+#include <atomic>
+
 namespace fk {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -129,6 +131,24 @@ struct SegParams {
     float* psums;
     const int32_t* poff;
 };
+
+// Raises a kernel's dynamic LDS limit to `bytes` once per device (the
+// attribute is a property of the function on the current device).  `rec` is
+// the kernel's own record: one bit per device ordinal below 64 (others set
+// the attribute on every launch).
+struct LdsAttr {
+    std::atomic<uint64_t> done{0};
+};
+inline hipError_t ensure_lds(LdsAttr& rec, const void* kern, int bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit && (rec.done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) rec.done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 
 // ---- launchers (return hipSuccess or the launch error) ----------------------
 hipError_t launch_fill_u32(uint32_t* ptr, int64_t n, uint32_t value, hipStream_t s);

@@ -464,13 +464,9 @@ hipError_t launch_assign_t(const void* X, const void* C, const float* bias, int3
     static_assert(lds <= kLdsBytes, "LDS budget");
     constexpr int PTS = kAssignWaves * NB * 32;
     auto kern = k_assign<T, Q, NB, VEC, EXACT, SMALLK>;
-    static bool attr_set = false;  // one attribute call per instantiation and process
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static LdsAttr attr;
+    hipError_t e = ensure_lds(attr, reinterpret_cast<const void*>(kern), lds);
+    if (e != hipSuccess) return e;
     // one workgroup per item
     const int64_t grid = B * ((N + PTS - 1) / PTS);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kAssignWaves * kWave), lds, s,

@@ -437,12 +437,9 @@ hipError_t launch_assign16_t(const void* X, const void* C, const float* bias, in
         kern = reinterpret_cast<const void*>(k_scores16<T, S, NP, VEC, EXACT, SMALLK>);
     else
         kern = reinterpret_cast<const void*>(k_assign16<T, S, NP, VEC, EXACT, SMALLK, W>);
-    static bool attr_set = false;  // one attribute call per instantiation and process
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static LdsAttr attr;
+    hipError_t e = ensure_lds(attr, kern, lds);
+    if (e != hipSuccess) return e;
     const int64_t items = B * ((N + PTS - 1) / PTS);
     const dim3 grid((unsigned)(grid_wgs > 0 && grid_wgs < items ? grid_wgs : items));
     if constexpr (MAT)

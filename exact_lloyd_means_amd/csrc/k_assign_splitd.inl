@@ -234,13 +234,9 @@ hipError_t launch_assign_splitd(const void* X, const void* C, const float* bias,
     const Kern kerns[4] = {k_assign_splitd<T, false, false>, k_assign_splitd<T, false, true>,
                            k_assign_splitd<T, true, false>, k_assign_splitd<T, true, true>};
     const Kern kern = kerns[variant];
-    static bool attr_set[4] = {false, false, false, false};
-    if (!attr_set[variant]) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set[variant] = true;
-    }
+    static LdsAttr attr[4];
+    hipError_t e = ensure_lds(attr[variant], reinterpret_cast<const void*>(kern), (int)lds);
+    if (e != hipSuccess) return e;
     const dim3 grid((unsigned)((N + kSdP - 1) / kSdP), (unsigned)B);
     hipLaunchKernelGGL(kern, grid, dim3(kSdWaves * kWave), lds, s, static_cast<const T*>(X),
                        static_cast<const T*>(C), bias, labels, min_dist, N, K, d);
