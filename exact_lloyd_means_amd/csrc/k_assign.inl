@@ -200,9 +200,13 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
     // re-reads the last tile) so the loop has no branches around them.
     int crow[PER], ccol[PER];
     uint32_t goff[PER];
+    // A tile of fewer chunks than threads (d <= 16): each chunk is loaded
+    // and stored by NT / CHUNKS threads (same value, same place), so no
+    // thread waits behind a branch and the tile loop stays one block.
+    static_assert(CHUNKS >= NT || NT % CHUNKS == 0, "whole copies of the tile");
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-        const int c = tid + u * NT;
+        const int c = CHUNKS < NT ? tid % CHUNKS : tid + u * NT;
         crow[u] = c / RC;
         ccol[u] = c % RC;
         const int cofs = EXACT ? ccol[u] * V : min(ccol[u] * V, d - V);
@@ -248,7 +252,7 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
             const char* base = reinterpret_cast<const char*>(Cb + (int64_t)tbase * d);
 #pragma unroll
             for (int u = 0; u < PER; ++u) {
-                if (CHUNKS % NT == 0 || u * NT + tid < CHUNKS) {
+                if (CHUNKS % NT == 0 || CHUNKS < NT || u * NT + tid < CHUNKS) {
                     if constexpr (SMALLK || !VEC) {
                         st.v[u] = load_chunk<T, VEC>(Cb, tbase + crow[u], K, d, ccol[u] * V);
                     } else {
@@ -267,7 +271,7 @@ void k_assign(const T* __restrict__ X, const T* __restrict__ C, const float* __r
         auto sstore = [&](int buf, const Staged& st) {
 #pragma unroll
             for (int u = 0; u < PER; ++u)
-                if (CHUNKS % NT == 0 || u * NT + tid < CHUNKS)
+                if (CHUNKS % NT == 0 || CHUNKS < NT || u * NT + tid < CHUNKS)
                     *reinterpret_cast<u32x4*>(s_tile + buf * TILEB + crow[u] * ROWB +
                                               ccol[u] * 16) = st.v[u];
             // every thread stores its bias value (identical stores per slot),
