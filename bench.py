@@ -154,26 +154,29 @@ def main() -> int:
     fk.fk_centroid_bias(Cq, bias)
 
     def step(g, e=None):
+        """One Lloyd iteration of group g.  e: timing events recorded before
+        and after the assign (and, with several groups, after the update).
+        With one group the update of this step ends where the next step's
+        first event (or the closing event) is recorded, so a step adds only
+        two markers to the stream."""
         sl = grp[g]
         with torch.cuda.stream(streams[g]):
-            if e:
-                e[0].record()
-                e[1].record()
             if G > 1 and args.schedule == "chain" and last[0] is not None:
                 streams[g].wait_event(last[0])
             if e:
-                e[4].record()
+                e[0].record()
             fk.fk_assign_with_bias(X[sl], Cq[sl], bias[sl], labels[sl])
             if e:
-                e[2].record()
-            chain[g].record()
-            last[0] = chain[g]
+                e[1].record()
+            if G > 1:
+                chain[g].record()
+                last[0] = chain[g]
             # in place: C_prev and C_next alias; the RNE copy and its bias feed
             # the next assign
             fk.fk_update_bias(X[sl], labels[sl], C[sl], C[sl], Cq[sl] if fmt != "f32" else None,
                               counts[sl], bias[sl], ws=ws[g])
-            if e:
-                e[3].record()
+            if e and G > 1:
+                e[2].record()
 
     log(f"[bench] {G} stream group(s) of {Hg} problems ({args.schedule}); "
         f"warmup {args.warmup} steps")
@@ -182,8 +185,10 @@ def main() -> int:
             step(g)
     torch.cuda.synchronize()
 
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(G)]
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2 if G == 1 else 3)]
+            for _ in range(G)]
            for _ in range(args.steps)]
+    tail = [torch.cuda.Event(enable_timing=True) for _ in range(G)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     log(f"[bench] timing {args.steps} steps")
@@ -196,14 +201,20 @@ def main() -> int:
     for s_ in range(args.steps):
         for g in range(G):
             step(g, evs[s_][g])
-    for st in streams:
+    for g, st in enumerate(streams):
+        tail[g].record(st)
         main_stream.wait_stream(st)
     end.record(main_stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
-    assign_ms = [e[4].elapsed_time(e[2]) for row in evs for e in row]
-    update_ms = [e[2].elapsed_time(e[3]) for row in evs for e in row]
+    assign_ms = [e[0].elapsed_time(e[1]) for row in evs for e in row]
+    # update of step s, group g: from its assign's end to the next step's
+    # start on the same stream
+    update_ms = [evs[s_][g][1].elapsed_time(evs[s_][g][2] if G > 1 else
+                                            evs[s_ + 1][g][0] if s_ + 1 < args.steps
+                                            else tail[g])
+                 for s_ in range(args.steps) for g in range(G)]
     log(f"[bench] {args.steps} steps: {total_ms:.3f} ms (events), {wall * 1e3:.3f} ms (wall)")
 
     if args.copy_calibration:
