@@ -478,21 +478,31 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(
 }
 
 // The same scatter for K <= kWaveBinsMax without barriers between the
-// waves: wave w takes the 1024 consecutive elements i0 + 1024 w + [0, 1024)
-// in 16 rounds of 64.  A first pass counts each wave's labels (the 16-bit
-// counts of two waves share a 32-bit LDS word), the counts become per-wave
-// exclusive prefixes, and a second pass ranks each round's lanes by ballot
-// match and advances the wave's own 16-bit cursor with one LDS atomic per
-// label group; the waves' ranges and the rounds inside a wave are in index
-// order, so the scatter is stable.
+// waves: each of the NW waves of the workgroup takes kSortTile / NW
+// consecutive elements of the tile, in rounds of 64.  A first pass counts
+// each wave's labels (the 16-bit counts of waves 2j and 2j+1 share the
+// 32-bit LDS word j of the label), the counts become per-wave exclusive
+// prefixes, and a second pass ranks each round's lanes by ballot match and
+// advances the wave's own 16-bit cursor with one LDS atomic per label group;
+// the waves' ranges and the rounds inside a wave are in index order, so the
+// scatter is stable.  More waves mean fewer dependent rounds per wave (a
+// round is a chain of ballots, an LDS atomic and a shuffle).
 constexpr int64_t kWaveBinsMax = 4096;
-constexpr int kWaveRange = kSortTile / (kBlock / kWave);  // elements per wave
-__global__ __launch_bounds__(kBlock) void k_tile_scatter_w(
+constexpr int kScatterWaves = 16;
+template <int NW>
+constexpr int scatter_w_lds(int64_t K) {
+    return (int)((1 + NW / 2) * K * (int64_t)sizeof(int32_t));
+}
+template <int NW>
+__global__ __launch_bounds__(NW * kWave) void k_tile_scatter_w(
     const int32_t* __restrict__ labels, const int32_t* __restrict__ th,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_idx,
     const int32_t* __restrict__ counts, float* __restrict__ sums, int32_t* __restrict__ arrive,
     int64_t N, int64_t K, int64_t T, int64_t d, int xcd_map, int nbits) {
-    extern __shared__ int32_t s_mem[];  // base [K] | cursors of waves 0,1 [K] | of waves 2,3 [K]
+    constexpr int kRange = kSortTile / NW;  // elements per wave
+    constexpr int kPer = kRange / kWave;    // rounds per wave
+    static_assert(NW % 2 == 0 && kRange % kWave == 0 && kRange < 65536, "16-bit cursors");
+    extern __shared__ int32_t s_mem[];  // base [K] | cursor word j of every label [NW/2][K]
     int32_t* s_base = s_mem;
     uint32_t* s_cur = reinterpret_cast<uint32_t*>(s_mem + K);
     int64_t b, t;
@@ -507,40 +517,45 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter_w(
     if (sums) clear_multi_rows(counts + b * K, sums + b * K * d, arrive + b * K, K, d, t, T);
     const int32_t* pre = th + (b * T + t) * (K + 1);
     const int32_t* off = offsets + b * (K + 1);
-    for (int64_t k = threadIdx.x; k < K; k += kBlock) {
+    for (int64_t k = threadIdx.x; k < K; k += NW * kWave) {
         s_base[k] = off[k] + pre[k];
-        s_cur[k] = 0u;
-        s_cur[K + k] = 0u;
+#pragma unroll
+        for (int j = 0; j < NW / 2; ++j) s_cur[j * K + k] = 0u;
     }
     __syncthreads();
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t w0 = t * kSortTile + (int64_t)wave * kWaveRange;
+    const int64_t w0 = t * kSortTile + (int64_t)wave * kRange;
     const int64_t i1 = min(t * kSortTile + (int64_t)kSortTile, N);
     const int32_t* lab = labels + b * N;
     int32_t* out = sorted_idx + b * N;
     uint32_t* cur = s_cur + (wave >> 1) * K;
     const uint32_t sh = 16u * (uint32_t)(wave & 1);
-    int32_t a[kSortPer];
+    int32_t a[kPer];
 #pragma unroll
-    for (int j = 0; j < kSortPer; ++j) {
+    for (int j = 0; j < kPer; ++j) {
         const int64_t i = w0 + j * kWave + lane;
         a[j] = i < i1 ? lab[i] : -1;
     }
 #pragma unroll
-    for (int j = 0; j < kSortPer; ++j)
+    for (int j = 0; j < kPer; ++j)
         if (a[j] >= 0 && a[j] < K) atomicAdd(&cur[a[j]], 1u << sh);
     __syncthreads();
-    for (int64_t k = threadIdx.x; k < K; k += kBlock) {
-        const uint32_t c01 = s_cur[k], c23 = s_cur[K + k];
-        const uint32_t p1 = c01 & 0xffffu, p2 = p1 + (c01 >> 16), p3 = p2 + (c23 & 0xffffu);
-        s_cur[k] = p1 << 16;
-        s_cur[K + k] = p2 | (p3 << 16);
+    // counts -> exclusive prefixes over the waves, in wave order
+    for (int64_t k = threadIdx.x; k < K; k += NW * kWave) {
+        uint32_t run = 0;
+#pragma unroll
+        for (int j = 0; j < NW / 2; ++j) {
+            const uint32_t c = s_cur[j * K + k];
+            const uint32_t lo = c & 0xffffu;
+            s_cur[j * K + k] = run | ((run + lo) << 16);
+            run += lo + (c >> 16);
+        }
     }
     __syncthreads();
     const uint64_t below = lane ? ~0ull >> (64 - lane) : 0ull;
 #pragma unroll
-    for (int j = 0; j < kSortPer; ++j) {
+    for (int j = 0; j < kPer; ++j) {
         const int64_t i = w0 + j * kWave + lane;
         const int32_t v = a[j];
         const bool valid = v >= 0 && v < K;
@@ -702,8 +717,10 @@ __global__ __launch_bounds__(kDigits * kDigitGroups) void k_digit_colscan(
 
 // Stable scatter of one pass: element i of tile t goes to
 // dth[b][t][digit] + (its rank among the tile's elements of that digit, in
-// index order), with wave-private cursors as in k_tile_scatter_w (wave w
-// takes 1024 consecutive elements; two waves' 16-bit counts share a word).
+// index order), with wave-private cursors as in k_tile_scatter_w (wave w of
+// four takes 1024 consecutive elements; two waves' 16-bit counts share a
+// word).
+constexpr int kWaveRange = kSortTile / (kBlock / kWave);  // elements per wave
 // keys_out may be null (last pass: values only).  With sums the workgroups
 // also clear the sum rows of multi-piece segments.
 __global__ __launch_bounds__(kBlock) void k_digit_scatter(
@@ -1325,12 +1342,17 @@ hipError_t launch_sort(const SortParams& sp, int64_t B, int64_t N, int64_t K, hi
         const int xcd_map = B % 8 == 0 && T * B < ((int64_t)1 << 31);
         const dim3 sgrid = xcd_map ? dim3((unsigned)(T * B)) : tiles;
         const int nbits = K > 1 ? 64 - __builtin_clzll((unsigned long long)(K - 1)) : 0;
-        if (K <= kWaveBinsMax)
-            hipLaunchKernelGGL(k_tile_scatter_w, sgrid, dim3(kBlock),
-                               (size_t)(3 * K) * sizeof(int32_t), s, sp.labels, sp.table,
-                               sp.offsets, sp.sorted_idx, sp.counts, sp.sums, sp.arrive, N, K, T,
-                               sp.d, xcd_map, nbits);
-        else
+        if (K <= kWaveBinsMax) {
+            constexpr int NW = kScatterWaves;
+            static LdsAttr attr;
+            const hipError_t e = ensure_lds(attr, reinterpret_cast<const void*>(k_tile_scatter_w<NW>),
+                                            scatter_w_lds<NW>(kWaveBinsMax));
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(k_tile_scatter_w<NW>, sgrid, dim3(NW * kWave),
+                               (size_t)scatter_w_lds<NW>(K), s, sp.labels, sp.table, sp.offsets,
+                               sp.sorted_idx, sp.counts, sp.sums, sp.arrive, N, K, T, sp.d,
+                               xcd_map, nbits);
+        } else
             hipLaunchKernelGGL(k_tile_scatter, sgrid, dim3(kBlock), (size_t)K * sizeof(int32_t), s,
                                sp.labels, sp.table, sp.offsets, sp.sorted_idx, sp.counts, sp.sums,
                                sp.arrive, N, K, T, sp.d, xcd_map, nbits);
