@@ -36,6 +36,46 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+class MarkerEvent:
+    """A timing-only HIP event: created with hipEventDisableSystemFence, so
+    recording it orders the stream and takes a timestamp but skips the
+    system-scope cache write-back and invalidate a default event performs
+    (the stream idles about 4.7 us per marker instead of 6 on MI355X).  The
+    events are read only after a device synchronisation.  Uses the HIP
+    runtime torch has already loaded (same soname)."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        if MarkerEvent._hip is None:
+            MarkerEvent._hip = ctypes.CDLL("libamdhip64.so.7")
+        self._ct = ctypes
+        self.ev = ctypes.c_void_p()
+        rc = MarkerEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.ev),
+                                                      MarkerEvent.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream=None):
+        import torch
+        st = stream if stream is not None else torch.cuda.current_stream()
+        rc = MarkerEvent._hip.hipEventRecord(self.ev, self._ct.c_void_p(st.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, other: "MarkerEvent") -> float:
+        ms = self._ct.c_float()
+        rc = MarkerEvent._hip.hipEventElapsedTime(self._ct.byref(ms), self.ev, other.ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if MarkerEvent._hip is not None and self.ev:
+            MarkerEvent._hip.hipEventDestroy(self.ev)
+
+
 def assign_sources_hash() -> str:
     h = hashlib.sha256()
     for f in ("k_assign.inl", "k_assign16.inl", "k_assign_splitd.inl", "k_assign_f16.hip",
@@ -185,10 +225,11 @@ def main() -> int:
             step(g)
     torch.cuda.synchronize()
 
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2 if G == 1 else 3)]
-            for _ in range(G)]
+    # per-step markers without the system-scope fence; the closing events
+    # (start/end, for the whole-job rate) are ordinary ones
+    evs = [[[MarkerEvent() for _ in range(2 if G == 1 else 3)] for _ in range(G)]
            for _ in range(args.steps)]
-    tail = [torch.cuda.Event(enable_timing=True) for _ in range(G)]
+    tail = [MarkerEvent() for _ in range(G)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     log(f"[bench] timing {args.steps} steps")
