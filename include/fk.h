@@ -48,7 +48,9 @@
  *           calling thread.  Faults inside kernels surface at the caller's
  *           next synchronisation.
  *  Limits   N, K <= 2^31 - 2; d <= 65536.  Inputs must be finite, and
- *           |c|^2 must be finite in fp32; otherwise labels are undefined.
+ *           |c|^2 must be finite in fp32; otherwise labels are undefined
+ *           (but stay in [0, K)).  A point with a non-finite coordinate
+ *           does not change the labels of the other points.
  */
 #ifndef FK_H
 #define FK_H

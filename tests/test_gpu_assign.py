@@ -141,3 +141,31 @@ def test_assign_with_bias_matches_assign(dt):
     cc = oracle.decode(to_storage(C), dt).astype(np.float64)
     ref = -0.5 * (cc ** 2).sum(-1)
     assert np.allclose(bias.cpu().numpy(), ref, rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("dt", DT)
+@pytest.mark.parametrize("shape", [(2, 700, 90, 128), (1, 600, 300, 1024), (1, 300, 20, 40)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_nonfinite_points_leave_the_others_alone(dt, shape):
+    """Labels of points with NaN or infinite coordinates are undefined, but
+    they stay in [0, K) and every finite point still gets its oracle label
+    (each point's running minimum is its own; resident, split-d and
+    element-load kernels)."""
+    B, N, K, d = shape
+    g = torch.Generator().manual_seed(N + K + d)
+    X = torch.randn((B, N, d), generator=g)
+    C = torch.randn((B, K, d), generator=g) * 1.2
+    bad = torch.zeros((B, N), dtype=torch.bool)
+    bad[:, 3::17] = True
+    X[:, 3::17, 5] = float("nan")
+    X[:, 10::17] = float("inf")
+    bad[:, 10::17] = True
+    X[:, 12::17, 0] = float("-inf")
+    bad[:, 12::17] = True
+    X = X.to(TORCH[dt]).cuda()
+    C = C.to(TORCH[dt]).cuda()
+    labels, _ = run_assign(X, C)
+    lab = labels.cpu()
+    assert int(lab.min()) >= 0 and int(lab.max()) < K
+    rows = np.flatnonzero(~bad.reshape(-1).numpy())
+    check_labels(labels, X, C, rows=rows)
