@@ -844,16 +844,18 @@ __device__ inline RowPart<T, EPL> load_row_part_buf(__amdgpu_buffer_rsrc_t rsrc,
     return r;
 }
 
-// Rows gathered per batch: at most 32, and so that the loaded values fit in
-// about 64 VGPRs.  A piece is a chain of dependent loads (piece table,
-// offsets, indices, rows, previous centroid), so waves per SIMD matter as
-// much as rows in flight per wave: 64 rows of 4 bytes per lane left three
-// waves per SIMD, 32 rows leave five (measured: 9 % faster at d = 128 fp16
-// with 64 points per cluster, 15-35 % faster with fewer).
+// Rows gathered per batch: at most 32, and at most 128 VGPRs of row data.
+// A piece is a chain of dependent loads (piece table, offsets, indices,
+// rows, previous centroid), so waves per SIMD matter as much as rows in
+// flight per wave: for 256-byte rows, 64 rows per batch left three waves per
+// SIMD and 32 rows leave five (9 % faster at d = 128 fp16 with 64 points per
+// cluster, 15-35 % faster with fewer).  Long rows want the opposite: at
+// d = 1024 bf16 (about 16 points per cluster) 16 rows per batch at two
+// waves per SIMD beat 8 rows at four by 32 %.
 template <typename T, int EPL>
 constexpr int seg_batch() {
     constexpr int regs = (EPL * (int)sizeof(T) + 3) / 4;
-    return regs >= 64 ? 1 : (64 / regs < 32 ? 64 / regs : 32);
+    return regs >= 128 ? 1 : (128 / regs < 32 ? 128 / regs : 32);
 }
 
 // Where the segment sums go.  FINAL: the fused finalize writes the new
@@ -932,6 +934,7 @@ __global__ __launch_bounds__(kBlock) void k_segment_sums(
     constexpr bool VEC = LD != 0;
     constexpr int RB = seg_batch<T, EPL>();
     constexpr int NV = kSegRun / kWave;  // index registers per lane
+    static_assert(kSegRun % RB == 0, "batches tile a piece exactly");
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t b = blockIdx.y;
