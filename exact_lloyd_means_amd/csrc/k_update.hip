@@ -146,8 +146,9 @@ __global__ __launch_bounds__(kBlock) void k_prepare(const float* __restrict__ C,
 // Pieces of the segment sums: every nonempty segment [off[k], off[k+1]) is
 // cut into pieces of at most kSegRun sorted positions, one wave each.  The
 // piece block of a problem holds P[0] = number of pieces, P[1 + j] = the
-// segment of piece j and P[1 + M + j] = its first position (M = capacity);
-// poff[k] is the first piece of segment k.
+// segment of piece j (-1 in the unused slots up to the capacity M) and
+// P[1 + M + j] = its first position; poff[k] is the first piece of
+// segment k.
 __device__ inline int32_t npieces_of(int32_t count) { return (count + kSegRun - 1) / kSegRun; }
 
 // Clears the sum rows and arrival counters of the segments with more than
@@ -369,10 +370,15 @@ __global__ __launch_bounds__(kBlock) void k_plan(const int32_t* __restrict__ cou
         po[k0 + i] = bp + s_po[i];
     }
     int32_t* P = pieces + b * (2 * M + 1);
-    if (blk == nblk - 1 && threadIdx.x == 0) {
-        off[K] = bc + tot_c;
-        po[K] = bp + tot_p;
-        P[0] = bp + tot_p;
+    if (blk == nblk - 1) {
+        if (threadIdx.x == 0) {
+            off[K] = bc + tot_c;
+            po[K] = bp + tot_p;
+            P[0] = bp + tot_p;
+        }
+        // unused slots: a segment-sums wave may read its slot without
+        // waiting for the count
+        for (int64_t j = bp + tot_p + threadIdx.x; j < M; j += kBlock) P[1 + j] = -1;
     }
     // pieces of this block: a segment of few pieces is written by the thread
     // that owns it; segments of many pieces (hot clusters) are listed and
@@ -873,10 +879,12 @@ struct SegOut {
     float* psums;          // [B][M][d] partial sums of pieces, or null (FINAL)
 };
 
-// Finalizes centroid row k of problem b from the lane's EPL sums.
-template <typename T, int EPL, bool VEC>
+// Finalizes centroid row k of problem b from the lane's EPL sums.  EARLY:
+// prev already holds the lane's elements of the previous centroid.
+template <typename T, int EPL, bool VEC, bool EARLY>
 __device__ inline void finalize_row(const SegOut<T>& o, int64_t b, int64_t K, int d, int64_t k,
-                                    int32_t count, const float (&s)[EPL], int e0) {
+                                    int32_t count, const float (&s)[EPL], int e0,
+                                    const float (&prev)[EPL]) {
     const int64_t base = (b * K + k) * d;
     if (!o.C_next) {
         // sums mode: the segment's sum row itself
@@ -892,7 +900,7 @@ __device__ inline void finalize_row(const SegOut<T>& o, int64_t b, int64_t K, in
         const int j = e0 + e;
         if (j < d) {
             const float c = s[e] / fn;
-            const float prev = o.C_prev[base + j];
+            const float pv = EARLY ? prev[e] : o.C_prev[base + j];
             o.C_next[base + j] = c;
             float cq = c;
             if (o.lowp) {
@@ -901,7 +909,7 @@ __device__ inline void finalize_row(const SegOut<T>& o, int64_t b, int64_t K, in
                 cq = to_f32(q);
             }
             cn = fmaf(cq, cq, cn);
-            const float m = c - prev;
+            const float m = c - pv;
             mv = fmaf(m, m, mv);
         }
     }
@@ -977,12 +985,17 @@ __global__ __launch_bounds__(kBlock) void k_segment_sums(
 
     const int32_t* __restrict__ P = pieces + b * (2 * M + 1);
     const int64_t j = (int64_t)blockIdx.x * (kBlock / kWave) + wave;
-    if (j >= P[0]) return;
+    // Long rows (EARLY): the piece's slot is read without waiting for the
+    // piece count (unused slots hold -1), and the indices and previous
+    // centroid are requested before the offsets resolve, so a piece costs
+    // one dependent round trip less (9 % at d = 1024 bf16 with 16 points
+    // per cluster).  With short rows the later, narrower requests measured
+    // 2-3 % faster.
+    constexpr bool EARLY = EPL * (int)sizeof(T) >= 16;
+    if (EARLY ? j >= M : j >= P[0]) return;
     const int32_t k = __builtin_amdgcn_readfirstlane(P[1 + j]);
     const int32_t p0 = __builtin_amdgcn_readfirstlane(P[1 + M + j]);
-    const int32_t s0 = __builtin_amdgcn_readfirstlane(off[k]);
-    const int32_t s1 = __builtin_amdgcn_readfirstlane(off[k + 1]);
-    const int n = min(kSegRun, s1 - p0);  // rows of this piece
+    if (EARLY && k < 0) return;
     const T* __restrict__ Xb = X + b * N * d;
     __amdgpu_buffer_rsrc_t rsrc;
     if constexpr (LD == 2)
@@ -991,9 +1004,33 @@ __global__ __launch_bounds__(kBlock) void k_segment_sums(
     const int32_t rowb = d * (int32_t)sizeof(T);
     const int32_t lane_off = (active ? e0 : 0) * (int32_t)sizeof(T);
     int32_t vidx[NV];
+    float prev[EPL];
+    int32_t s0, s1;
+    int n;  // rows of this piece
+    if constexpr (EARLY) {
+        // positions past the piece read whatever index follows (clamped to
+        // the array); never used
 #pragma unroll
-    for (int v = 0; v < NV; ++v)
-        vidx[v] = sorted_idx[b * N + p0 + min(v * kWave + lane, n - 1)];
+        for (int v = 0; v < NV; ++v)
+            vidx[v] = sorted_idx[b * N + min((int64_t)p0 + v * kWave + lane, N - 1)];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            prev[e] = FINAL && o.C_next && active && (VEC || e0 + e < d)
+                          ? o.C_prev[(b * K + k) * d + e0 + e]
+                          : 0.f;
+        s0 = __builtin_amdgcn_readfirstlane(off[k]);
+        s1 = __builtin_amdgcn_readfirstlane(off[k + 1]);
+        n = min(kSegRun, s1 - p0);
+    } else {
+        s0 = __builtin_amdgcn_readfirstlane(off[k]);
+        s1 = __builtin_amdgcn_readfirstlane(off[k + 1]);
+        n = min(kSegRun, s1 - p0);
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+            vidx[v] = sorted_idx[b * N + p0 + min(v * kWave + lane, n - 1)];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) prev[e] = 0.f;
+    }
 
     float acc[EPL];
 #pragma unroll
@@ -1034,7 +1071,7 @@ __global__ __launch_bounds__(kBlock) void k_segment_sums(
 
     const int32_t count = s1 - s0;
     if (FINAL && count <= kSegRun) {
-        finalize_row<T, EPL, VEC>(o, b, K, d, k, count, acc, e0);
+        finalize_row<T, EPL, VEC, EARLY>(o, b, K, d, k, count, acc, e0, prev);
         return;
     }
     if (FINAL && o.psums) {
@@ -1071,7 +1108,7 @@ __global__ __launch_bounds__(kBlock) void k_segment_sums(
                 t[e] = active && (VEC || e0 + e < d)
                            ? __hip_atomic_load(dst + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                            : 0.f;
-            finalize_row<T, EPL, VEC>(o, b, K, d, k, count, t, e0);
+            finalize_row<T, EPL, VEC, EARLY>(o, b, K, d, k, count, t, e0, prev);
         }
     } else if (active) {
 #pragma unroll
