@@ -77,10 +77,13 @@ class MarkerEvent:
 
 
 def assign_sources_hash() -> str:
+    """Hash of everything that decides the assign kernels' code: their
+    sources and the build script (compiler flags)."""
     h = hashlib.sha256()
-    for f in ("k_assign.inl", "k_assign16.inl", "k_assign_splitd.inl", "k_assign_f16.hip",
-              "k_assign_bf16.hip", "k_assign_f32.hip"):
-        with open(os.path.join(ROOT, "exact_lloyd_means_amd", "csrc", f), "rb") as fh:
+    for f in ("csrc/k_assign.inl", "csrc/k_assign16.inl", "csrc/k_assign_splitd.inl",
+              "csrc/k_assign_f16.hip", "csrc/k_assign_bf16.hip", "csrc/k_assign_f32.hip",
+              "build.py"):
+        with open(os.path.join(ROOT, "exact_lloyd_means_amd", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 

@@ -33,10 +33,16 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 
+# The distance kernels: LLVM's ILP-first machine scheduler for the regions
+# between their scheduling barriers (1-4 % faster on every assign workload,
+# measured against the default strategy in the same process).
+EXTRA = {src: ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+         for src in ("k_assign_f16.hip", "k_assign_bf16.hip", "k_assign_f32.hip", "k_tune.hip")}
+
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

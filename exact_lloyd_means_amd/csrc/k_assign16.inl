@@ -281,6 +281,12 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
             u32x4 nx[P];
             floatx4 nbv[RB];
             __builtin_amdgcn_sched_barrier(0);
+            // Higher issue priority for the matrix and epilogue part of the
+            // tile, back to normal for the staging stores and the barrier:
+            // when both waves of a SIMD are ready, the one feeding the
+            // matrix unit goes first (1-4 % faster on the B=32, K=1024
+            // workloads).
+            __builtin_amdgcn_s_setprio(1);
             if constexpr (MAT)
                 mat_store(t, prv);
             else
@@ -335,6 +341,7 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
             for (int q = 0; q < P; ++q) a[q] = nx[q];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) bv[rb] = nbv[rb];
+            __builtin_amdgcn_s_setprio(0);
             sstore(b3, st[(i & 1) ^ 1]);
             __syncthreads();
         };
