@@ -147,8 +147,9 @@ def main() -> int:
         return summarize(args.summarize)
 
     if args.gpus != 1:
-        msg = ("this build runs on one GPU only: pass --gpus 1 (the problems of a batch are "
-               "independent, so more GPUs would each take B/G problems; not built here)")
+        msg = ("bench.py measures one GPU: pass --gpus 1 (the problems of a batch are "
+               "independent, so more GPUs would each take B/G problems; that path does not "
+               "exist in this library)")
         if int(os.environ.get("RANK", "0")) == 0:
             log(msg)
         return 2
