@@ -137,6 +137,10 @@ void k_assign_splitd(const T* __restrict__ X, const T* __restrict__ C,
 #pragma unroll
                 for (int u = 0; u < LPT; ++u) pre[u] = load_slot(u, kbase, ch + 1);
             }
+            // 16-bit: raised issue priority for the chunk's matrix part,
+            // normal for the staging stores and the barrier (2 % faster at
+            // d = 1024 bf16; the fp32 form measured 1 % slower with it)
+            if constexpr (sizeof(T) == 2) __builtin_amdgcn_s_setprio(1);
             const char* xs = s_stage + buf * kSdStage;
             const char* cs = xs + kSdP * kSdRowB;
 #pragma unroll
@@ -157,6 +161,7 @@ void k_assign_splitd(const T* __restrict__ X, const T* __restrict__ C,
                             acc[rb][cb] = M::step(a[rb], x[cb],
                                                   (ch == 0 && s == 0 && e == 0) ? bv[rb] : acc[rb][cb], e);
             }
+            if constexpr (sizeof(T) == 2) __builtin_amdgcn_s_setprio(0);
             if (more) {
 #pragma unroll
                 for (int u = 0; u < LPT; ++u) store_slot(u, buf ^ 1, pre[u]);
