@@ -285,7 +285,8 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
             // tile, back to normal for the staging stores and the barrier:
             // when both waves of a SIMD are ready, the one feeding the
             // matrix unit goes first (1-4 % faster on the B=32, K=1024
-            // workloads).
+            // workloads, 1-2 % of it from the ILP-first scheduler the build
+            // selects for this unit).
             __builtin_amdgcn_s_setprio(1);
             if constexpr (MAT)
                 mat_store(t, prv);
