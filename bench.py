@@ -49,7 +49,14 @@ class MarkerEvent:
     def __init__(self):
         import ctypes
         if MarkerEvent._hip is None:
-            MarkerEvent._hip = ctypes.CDLL("libamdhip64.so.7")
+            for name in ("libamdhip64.so.7", "libamdhip64.so"):
+                try:
+                    MarkerEvent._hip = ctypes.CDLL(name)
+                    break
+                except OSError:
+                    continue
+            if MarkerEvent._hip is None:
+                raise RuntimeError("HIP runtime library not found")
         self._ct = ctypes
         self.ev = ctypes.c_void_p()
         rc = MarkerEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.ev),
