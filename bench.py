@@ -42,21 +42,20 @@ class MarkerEvent:
     system-scope cache write-back and invalidate a default event performs
     (the stream idles about 4.7 us per marker instead of 6 on MI355X).  The
     events are read only after a device synchronisation.  Uses the HIP
-    runtime torch has already loaded (same soname)."""
+    runtime torch has already loaded."""
     _hip = None
     DISABLE_SYSTEM_FENCE = 0x20000000
 
     def __init__(self):
         import ctypes
         if MarkerEvent._hip is None:
-            for name in ("libamdhip64.so.7", "libamdhip64.so"):
-                try:
-                    MarkerEvent._hip = ctypes.CDLL(name)
-                    break
-                except OSError:
-                    continue
-            if MarkerEvent._hip is None:
-                raise RuntimeError("HIP runtime library not found")
+            # the copy already mapped into this process (torch's), never a
+            # second runtime
+            with open("/proc/self/maps") as f:
+                paths = [ln.split()[-1] for ln in f if "libamdhip64.so" in ln]
+            if not paths:
+                raise RuntimeError("no HIP runtime loaded in this process")
+            MarkerEvent._hip = ctypes.CDLL(paths[0])
         self._ct = ctypes
         self.ev = ctypes.c_void_p()
         rc = MarkerEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.ev),
