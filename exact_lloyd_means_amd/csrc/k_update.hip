@@ -951,33 +951,41 @@ __global__ __launch_bounds__(kBlock) void k_segment_sums(
     const bool active = e0 < d;
 
     if ((int64_t)blockIdx.x >= piece_wgs) {
-        // empty segments: keep the previous centroid (FINAL only)
+        // empty segments keep the previous centroid (FINAL only): a wave
+        // checks 64 consecutive segments with one coalesced read of the
+        // offsets, then handles the empty ones (usually none) in turn
         if constexpr (FINAL) {
-            const int64_t k = ((int64_t)blockIdx.x - piece_wgs) * (kBlock / kWave) + wave;
-            if (k >= K || off[k + 1] != off[k]) return;
-            const int64_t base = (b * K + k) * d;
-            if (!o.C_next) {  // sums mode: an empty segment sums to zero
-                for (int j = lane; j < d; j += kWave) o.sums[base + j] = 0.f;
-                return;
-            }
-            float cn = 0.f;
-            const int E = row_part(d);
-            for (int e = 0; e < E; ++e) {
-                const int j = lane * E + e;
-                if (j >= d) break;
-                const float c = o.C_prev[base + j];
-                o.C_next[base + j] = c;
-                float cq = c;
-                if (o.lowp) {
-                    const T q = (T)c;
-                    o.lowp[base + j] = q;
-                    cq = to_f32(q);
+            const int64_t k0 =
+                (((int64_t)blockIdx.x - piece_wgs) * (kBlock / kWave) + wave) * kWave;
+            const int64_t kl = k0 + lane;
+            uint64_t m = __ballot(kl < K && off[kl + 1] == off[kl]);
+            while (m) {
+                const int64_t k = k0 + __ffsll((unsigned long long)m) - 1;
+                m &= m - 1;
+                const int64_t base = (b * K + k) * d;
+                if (!o.C_next) {  // sums mode: an empty segment sums to zero
+                    for (int j = lane; j < d; j += kWave) o.sums[base + j] = 0.f;
+                    continue;
                 }
-                cn = fmaf(cq, cq, cn);
-            }
-            if (o.bias) {
-                cn = wave_sum(cn);
-                if (lane == 0) o.bias[b * K + k] = -0.5f * cn;
+                float cn = 0.f;
+                const int E = row_part(d);
+                for (int e = 0; e < E; ++e) {
+                    const int j = lane * E + e;
+                    if (j >= d) break;
+                    const float c = o.C_prev[base + j];
+                    o.C_next[base + j] = c;
+                    float cq = c;
+                    if (o.lowp) {
+                        const T q = (T)c;
+                        o.lowp[base + j] = q;
+                        cq = to_f32(q);
+                    }
+                    cn = fmaf(cq, cq, cn);
+                }
+                if (o.bias) {
+                    cn = wave_sum(cn);
+                    if (lane == 0) o.bias[b * K + k] = -0.5f * cn;
+                }
             }
         }
         return;
@@ -1231,7 +1239,7 @@ hipError_t segment_sums_t(const void* X, const int32_t* sorted_idx, const int32_
     const int epl = (d + kWave - 1) / kWave;
     const int64_t M = piece_capacity(N, K);
     const int64_t piece_wgs = (M + (kBlock / kWave) - 1) / (kBlock / kWave);
-    const int64_t row_wgs = sp.final ? (K + (kBlock / kWave) - 1) / (kBlock / kWave) : 0;
+    const int64_t row_wgs = sp.final ? (K + kBlock - 1) / kBlock : 0;  // 64 segments per wave
     const dim3 grid((unsigned)(piece_wgs + row_wgs), (unsigned)B);
     SegOut<T> o{sp.sums, sp.arrive, sp.C_prev, sp.C_next, static_cast<T*>(sp.lowp), sp.bias,
                 sp.move, sp.final ? sp.psums : nullptr};
