@@ -83,6 +83,7 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
     constexpr int kSlots = S * RB;
     constexpr int P = kSlots <= 2 ? kSlots : 2;        // fragments prefetched for the next tile
     constexpr int kBiasSlot = kSlots > 3 ? kSlots - 3 : 0;
+    constexpr int kEpiSteps = 12 * NP;                 // epilogue steps per tile (epi_op)
     static_assert(!EXACT || VEC, "EXACT implies VEC");
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -242,6 +243,43 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
             }
         };
 
+        // The same decision as epi_row over the tile's 8 rows, in fewer
+        // vector operations: the tile maximum (with the running best) by a
+        // tree of three-input maxima, the lowest row holding it by a
+        // descending chain of compare-and-selects, then one update.  The
+        // maximum of finite and infinite scores is one of them, NaN scores
+        // are passed over by the maxima and equal nothing, and best never
+        // becomes NaN, so the row found is the first whose score exceeds
+        // everything before it, which is what strict > over ascending rows
+        // keeps (a -0/+0 tie may leave best with the other sign of zero,
+        // which compares equal).  Twelve steps per point block, one block
+        // after the other, so each block's scores die early: 4 maxima, 7
+        // chain links, 1 update.
+        static_assert(RB == 2, "8 rows per lane and tile");
+        float h0, h1, h2, tm;
+        int32_t ti;
+        auto epi_op = [&](const floatx4(&sc)[RB][NP], int op, int32_t kb) {
+            const int np = op / 12, j = op % 12;
+            auto sv = [&](int r) { return sc[r >> 2][np][r & 3]; };
+            if (j == 0) {
+                h0 = fmaxf(fmaxf(sv(0), sv(1)), sv(2));
+            } else if (j == 1) {
+                h1 = fmaxf(fmaxf(sv(3), sv(4)), sv(5));
+            } else if (j == 2) {
+                h2 = fmaxf(fmaxf(sv(6), sv(7)), best[np]);
+            } else if (j == 3) {
+                tm = fmaxf(fmaxf(h0, h1), h2);
+            } else if (j < 11) {
+                const int r = 10 - j;  // rows 6 .. 0
+                const int32_t keep = r == 6 ? 16 + 3 : ti;
+                ti = sv(r) == tm ? 16 * (r >> 2) + (r & 3) : keep;
+            } else {
+                const bool up = tm > best[np];
+                best[np] = tm;
+                bidx[np] = up ? kb + ti : bidx[np];
+            }
+        };
+
         floatx4 acc[2][RB][NP];
         Staged st[2];
         u32x4 a[kSlots];  // centroid fragments of the tile whose MFMAs run next
@@ -288,42 +326,25 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
             // workloads, 1-2 % of it from the ILP-first scheduler the build
             // selects for this unit).
             __builtin_amdgcn_s_setprio(1);
-            if constexpr (MAT)
-                mat_store(t, prv);
-            else
-                epi_begin();
+            if constexpr (MAT) mat_store(t, prv);
+            const int32_t kb_prv = tile_base(t);
 #pragma unroll
             for (int sl = 0; sl < kSlots; ++sl) {
                 const int s = sl / RB, rb = sl % RB;
-                // The slot's rows of the previous tile's epilogue are spread
-                // over its MFMAs so they issue while the matrix unit works:
-                // per row, one group of compares for all point blocks (masks
-                // kept in SGPRs), then two groups of selects; group g follows
-                // MFMA g * NP / G.
-                bool upd[NP];
+                // The previous tile's epilogue (epi_op, 12 NP steps) is
+                // spread evenly over the tile's MFMAs so it issues while the
+                // matrix unit works.
                 static_for<0, NP>([&](auto Q) {
                     constexpr int q = decltype(Q)::value;
                     cur[rb][q] = M::step(a[sl], xf[q][s], s == 0 ? bv[rb] : cur[rb][q]);
                     if constexpr (!MAT) {
-                        // rows r0 .. r1-1 of this slot, G groups
-                        static_for<0, 12>([&](auto GG) {
-                            constexpr int g = decltype(GG)::value;
-                            if (g >= 3 * (8 * (sl + 1) / kSlots - 8 * sl / kSlots)) return;
-                            const int G = 3 * (8 * (sl + 1) / kSlots - 8 * sl / kSlots);
-                            if (g * NP / G != q) return;
-                            const int r = 8 * sl / kSlots + g / 3, prb = r >> 2, pi = r & 3;
-                            if constexpr (g % 3 == 0) {
-#pragma unroll
-                                for (int np = 0; np < NP; ++np) upd[np] = prv[prb][np][pi] > m[np];
-                            } else {
-                                constexpr int lo = g % 3 == 1 ? 0 : NP / 2;
-                                constexpr int hi = g % 3 == 1 ? NP / 2 : NP;
-#pragma unroll
-                                for (int np = lo; np < hi; ++np) {
-                                    m[np] = upd[np] ? prv[prb][np][pi] : m[np];
-                                    rt[np] = upd[np] ? 16 * prb + pi : rt[np];
-                                }
-                            }
+                        constexpr int kMfmas = kSlots * NP;
+                        constexpr int kMost = (kEpiSteps + kMfmas - 1) / kMfmas;
+                        const int mi = sl * NP + q;
+                        const int lo = mi * kEpiSteps / kMfmas, hi = (mi + 1) * kEpiSteps / kMfmas;
+                        static_for<0, kMost>([&](auto O) {
+                            const int op = lo + decltype(O)::value;
+                            if (op < hi) epi_op(prv, op, kb_prv);
                         });
                     }
                     __builtin_amdgcn_sched_barrier(0);
@@ -337,7 +358,6 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
                 if (sl == kBiasSlot) bias_vec(b2, nbv);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if constexpr (!MAT) epi_end(t);
 #pragma unroll
             for (int q = 0; q < P; ++q) a[q] = nx[q];
 #pragma unroll
