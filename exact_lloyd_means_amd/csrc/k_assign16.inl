@@ -186,32 +186,6 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
                 bv[rb] = *reinterpret_cast<const floatx4*>(s_bias + buf * kAssignBK + 16 * rb + 4 * g);
         };
 
-        // Running (max score, lowest index) per point block; within a tile
-        // the candidate index is the row offset 16 rb + i of the lane's row
-        // group (an inline constant, -1 = no improvement in this tile); rows
-        // ascend with (rb, i), so strict > keeps the lowest index.
-        float m[NP];
-        int32_t rt[NP];
-        auto epi_begin = [&]() {
-#pragma unroll
-            for (int np = 0; np < NP; ++np) {
-                m[np] = best[np];
-                rt[np] = -1;
-            }
-        };
-        // row r = 4 rb + i of point block np
-        auto epi_one = [&](const floatx4 (&sc)[RB][NP], int r, int np) {
-            const int rb = r >> 2, i = r & 3;
-            const float s = sc[rb][np][i];
-            const bool keep = !(s > m[np]);
-            m[np] = keep ? m[np] : s;
-            rt[np] = keep ? rt[np] : 16 * rb + i;
-        };
-        // row r of all point blocks
-        auto epi_row = [&](const floatx4 (&sc)[RB][NP], int r) {
-#pragma unroll
-            for (int np = 0; np < NP; ++np) epi_one(sc, r, np);
-        };
         // MAT: lane (g, col) holds scores of centroids 16 rb + 4 g + i
         // (i = 0..3) of point col of each block
         auto mat_store = [&](int t, const floatx4(&sc)[RB][NP]) {
@@ -234,25 +208,19 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
                 }
             }
         };
-        auto epi_end = [&](int t) {
-            const int32_t kb = tile_base(t);
-#pragma unroll
-            for (int np = 0; np < NP; ++np) {
-                best[np] = m[np];
-                bidx[np] = rt[np] >= 0 ? kb + rt[np] : bidx[np];
-            }
-        };
-
-        // The same decision as epi_row over the tile's 8 rows, in fewer
-        // vector operations: the tile maximum (with the running best) by a
-        // tree of three-input maxima, the lowest row holding it by a
-        // descending chain of compare-and-selects, then one update.  The
-        // maximum of finite and infinite scores is one of them, NaN scores
-        // are passed over by the maxima and equal nothing, and best never
-        // becomes NaN, so the row found is the first whose score exceeds
-        // everything before it, which is what strict > over ascending rows
-        // keeps (a -0/+0 tie may leave best with the other sign of zero,
-        // which compares equal).  Twelve steps per point block, one block
+        // Running (max score, lowest index) per point block.  A tile gives
+        // each lane 8 rows of each point block, centroid 16 rb + 4 g + i
+        // of the tile for row r = 4 rb + i; rows ascend with the index, so
+        // the decision is that of a strict > over ascending rows against
+        // the running best.  It is taken in few vector operations: the tile
+        // maximum (with the running best) by a tree of three-input maxima,
+        // the lowest row holding it by a descending chain of
+        // compare-and-selects, then one update.  The maximum of finite and
+        // infinite scores is one of them, NaN scores are passed over by the
+        // maxima and equal nothing, and best never becomes NaN, so the row
+        // found is the first whose score exceeds everything before it (a
+        // -0/+0 tie may leave best with the other sign of zero, which
+        // compares equal).  Twelve steps per point block, one block
         // after the other, so each block's scores die early: 4 maxima, 7
         // chain links, 1 update.
         static_assert(RB == 2, "8 rows per lane and tile");
@@ -371,10 +339,8 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
                 mat_store(t, sc);
                 return;
             }
-            epi_begin();
-#pragma unroll
-            for (int r = 0; r < 8; ++r) epi_row(sc, r);
-            epi_end(t);
+            const int32_t kb = tile_base(t);
+            static_for<0, kEpiSteps>([&](auto O) { epi_op(sc, decltype(O)::value, kb); });
         };
         int t = 0;
         for (; t + 4 < ntiles; t += 4) {
