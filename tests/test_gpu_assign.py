@@ -64,6 +64,27 @@ def test_integer_ties_exact(dt, shape):
     assert np.array_equal(md.cpu().numpy().astype(np.float64), d1)
 
 
+@pytest.mark.parametrize("dt", DT)
+@pytest.mark.parametrize("B,N,K,d", [(2, 3000, 64, 16), (1, 2000, 100, 128), (1, 1500, 1000, 64),
+                                     (1, 700, 45, 256), (1, 500, 300, 1024)])
+def test_duplicate_centroids_take_the_lowest_copy(dt, B, N, K, d):
+    """Centroid k repeats centroid k mod 7, so copies tie exactly (same values,
+    same score) inside a tile, across tiles and in the overlapping last tile:
+    the lowest index rule puts every label below 7, whatever the rounding of
+    the scores.  Zero points (score = bias alone) are included."""
+    g = torch.Generator().manual_seed(B * 7 + N + K + d)
+    X = torch.randn((B, N, d), generator=g)
+    X[:, :5] = 0.0
+    base = torch.randn((B, 7, d), generator=g)
+    C = base[:, torch.arange(K) % 7]
+    X, C = X.to(TORCH[dt]).cuda(), C.to(TORCH[dt]).contiguous().cuda()
+    labels, md = run_assign(X, C)
+    lab = labels.cpu()
+    assert int(lab.min()) >= 0 and int(lab.max()) < 7
+    # and the copy chosen is the nearest of the 7 distinct centroids
+    check_labels(labels, X, C[:, :7].contiguous())
+
+
 CFG_SHRUNK = {1: dict(), 2: dict(B=2, N=8192), 3: dict(N=16384), 4: dict(N=3000, K=1100)}
 
 
