@@ -727,6 +727,33 @@ def summarize(argv) -> int:
                "assign_sources_sha256_16": assign_sources_hash()}
         print(json.dumps(rec, indent=1))
         return 0
+    if kind == "traffic-kernels":
+        # FETCH_SIZE / WRITE_SIZE of every library kernel (calibrated like
+        # 'traffic'), one record per kernel: MB per dispatch
+        fetch_csv, write_csv, workload, cmd = argv[1], argv[2], argv[3], " ".join(argv[4:])
+        per = {}
+        factors = {}
+        for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+            rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+            copy = [float(r["Counter_Value"]) for r in rows
+                    if "elementwise" in r["Kernel_Name"] and "Mul" in r["Kernel_Name"]]
+            copy = [v for v in copy if v > 0.5 * max(copy)]
+            factors[counter] = (1 << 20) / (sum(copy) / len(copy))
+            for r in rows:
+                name = _short_name(r["Kernel_Name"])
+                if not name.startswith("k_"):
+                    continue
+                per.setdefault(name, {}).setdefault(counter, []).append(float(r["Counter_Value"]))
+        kernels = {}
+        for name, cs in sorted(per.items()):
+            rec = {"dispatches": len(next(iter(cs.values())))}
+            for counter, vals in cs.items():
+                rec[f"{counter}_MB_per_dispatch"] = round(
+                    sum(vals) / len(vals) * 1024 * factors[counter] / 1e6, 3)
+            kernels[name] = rec
+        print(json.dumps({"workload": workload, "command": cmd,
+                          "calibration_factor": factors, "kernels": kernels}, indent=1))
+        return 0
     if kind == "counters":
         # SQ counters of the assign dispatches from several --pmc passes:
         # per-SIMD busy fractions against the GRBM clock count (summed over

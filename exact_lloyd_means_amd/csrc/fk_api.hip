@@ -243,6 +243,11 @@ fk_status fk_workspace_size(const fk_problem* p, int64_t chunk_points, size_t* b
     return FK_OK;
 }
 
+size_t fk_workspace_bytes(const fk_problem* p, int64_t chunk_points) {
+    size_t bytes = 0;
+    return fk_workspace_size(p, chunk_points, &bytes) == FK_OK ? bytes : 0;
+}
+
 fk_status fk_centroid_bias(const fk_problem* p, const void* C, float* bias, void* stream) {
     FK_CHECK(check_problem(p));
     FK_CHECK(check_ptr(C, "C"));

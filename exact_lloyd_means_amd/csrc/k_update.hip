@@ -9,15 +9,15 @@
 //
 // MI355X design:
 //  * The argsort is a counting sort, since keys are small integers in [0, K).
-//    Tiled form (K <= 16384 and a per-tile table of modest size): each
+//    Tiled form (K <= 16000 and a per-tile table of modest size): each
 //    workgroup histograms a tile of 4096 labels in LDS and writes the tile's
 //    counts; a column pass turns them into per-tile prefix counts; the
-//    scatter workgroup rescans the counts in LDS, so every label of its tile
-//    has a base position, and ranks its elements with LDS atomics.  No
-//    global atomics.  Otherwise (large K) the histogram uses global atomics
-//    and each scatter workgroup reserves one range per label with a single
-//    global atomic.  Order inside a segment is unspecified in both forms; the
-//    grouping is exact.
+//    scatter workgroup gives every label of its tile a base position from
+//    them and ranks its elements by lane order within each wave (ballots),
+//    so no global atomics are needed.  Larger K: counts from a histogram
+//    with global atomics and the argsort from least-significant-digit radix
+//    passes over 8-bit digits.  Both forms are stable: inside a segment the
+//    points keep increasing index order.
 //  * The gather-reduce gives every wave a fixed run of 256 sorted positions,
 //    so hot clusters spread over many waves.  The segment walk is
 //    wave-uniform (row indices come through readlane, segment boundaries
@@ -1109,7 +1109,12 @@ __global__ __launch_bounds__(kBlock) void k_segment_sums(
         if (lane == 0) prior = atomicAdd(o.arrive + b * K + k, 1);
         prior = __builtin_amdgcn_readfirstlane(prior);
         if (prior == npieces - 1) {
-            // every other piece added its sums before arriving
+            // Every other piece's adds returned before that piece arrived,
+            // so they were performed at the coherence point where this
+            // piece's adds and the arrival counter live.  The acquire fence
+            // (once per segment of several pieces) keeps the loads below
+            // from being served by a stale line in this wave's caches.
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             float t[EPL];
 #pragma unroll
             for (int e = 0; e < EPL; ++e)

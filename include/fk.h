@@ -117,6 +117,14 @@ const char* fk_last_error(void);
 fk_status fk_workspace_size(const fk_problem* p, int64_t chunk_points, size_t* bytes);
 
 /*
+ * fk_workspace_bytes -- the same size returned directly: bytes of device
+ * workspace for problem *p (chunk_points as in fk_workspace_size).  Returns
+ * 0 when the problem or chunk_points is invalid; fk_last_error() then says
+ * why.  No N x K term, as above.
+ */
+size_t fk_workspace_bytes(const fk_problem* p, int64_t chunk_points);
+
+/*
  * fk_centroid_bias -- the centroid term of the distance expansion
  * |x - c|^2 = |x|^2 + |c|^2 - 2 x.c (papernotes.org notes, 关键设计 1):
  * bias[b][k] = -0.5 * sum_j C[b][k][j]^2, accumulated in fp32 from the

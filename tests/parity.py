@@ -36,10 +36,14 @@ def to_storage(t: torch.Tensor) -> np.ndarray:
 
 
 def check_labels(gpu_labels: torch.Tensor, X: torch.Tensor, Cq: torch.Tensor,
-                 rows: np.ndarray | None = None, min_dist: torch.Tensor | None = None) -> dict:
+                 rows: np.ndarray | None = None, min_dist: torch.Tensor | None = None,
+                 keep_oracle_labels: bool = False) -> dict:
     """GPU labels (B, N) against the oracle's assignment of X to Cq (the
     centroids exactly as the GPU read them).  With rows, only those flattened
-    point ids are checked."""
+    point ids are checked.  The returned counts: n checked points, near_ties
+    (points excluded from the bit-exact rule by the gap test) and
+    excluded_diff (excluded points whose GPU label differs from the
+    oracle's); with keep_oracle_labels also the oracle's labels."""
     fmt = FMT[X.dtype]
     tau = TAU[fmt]
     Xs, Cs = to_storage(X), to_storage(Cq)
@@ -73,7 +77,10 @@ def check_labels(gpu_labels: torch.Tensor, X: torch.Tensor, Cq: torch.Tensor,
         N = X.shape[1]
         scale = xx + cn[(pts // N) * Kc + g]
         assert np.all(np.abs(md - dg) <= 1e-5 * scale + 1e-6), "min_dist off"
-    return {"n": int(lab.size), "near_ties": int((~strict).sum()), "excluded_diff": int(excl.size)}
+    out = {"n": int(lab.size), "near_ties": int((~strict).sum()), "excluded_diff": int(excl.size)}
+    if keep_oracle_labels:
+        out["oracle_labels"] = lab
+    return out
 
 
 def check_update(X: torch.Tensor, labels: torch.Tensor, C_prev: torch.Tensor,

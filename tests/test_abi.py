@@ -194,3 +194,16 @@ def test_last_error_is_per_call():
     assert first
     ok = fk.lib.fk_workspace_size(ctypes.byref(p), 0, ctypes.byref(ctypes.c_size_t()))
     assert ok == fk.FK_OK
+
+
+def test_workspace_bytes_matches_size():
+    for p in (P(), P(flags=fk.FK_DETERMINISTIC), P(B=3, N=5000, K=700, d=129, dtype=fk.FK_F32)):
+        assert fk.lib.fk_workspace_bytes(ctypes.byref(p), 0) == ws_size(p)
+        assert fk.lib.fk_workspace_bytes(ctypes.byref(p), 64) == fk.workspace_size(p, 64)
+
+
+def test_workspace_bytes_zero_on_error():
+    p = P(K=0)
+    assert fk.lib.fk_workspace_bytes(ctypes.byref(p), 0) == 0
+    assert b"sizes" in fk.lib.fk_last_error()
+    assert fk.lib.fk_workspace_bytes(ctypes.byref(P()), -1) == 0

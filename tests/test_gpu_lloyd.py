@@ -46,31 +46,43 @@ def test_lockstep(cfg):
         Cq = lowp if lowp is not None else C_next
 
 
-def test_fused_loop_matches_steps():
-    """fk_lloyd(T) runs the same kernels as T x (fk_assign, fk_update)."""
-    X, C0 = synth.make(2, B=2, N=4096)
-    X = X.cuda()
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_fused_loop_lockstep_oracle(dt):
+    """The 16-bit fk_lloyd loop against the oracle, one iteration per call:
+    each call rounds the fp32 centroids it is given to the input dtype
+    (nearest, ties to even), assigns and updates.  The labels must be the
+    oracle's assignment to the oracle's own RNE rounding of those centroids
+    (so a copy rounded any other way shows up as label differences), and
+    counts and centroids the oracle's update from those labels.  Then
+    fk_lloyd(T) in one call -- where every assignment after the first reads
+    the rounded copy and bias written by the previous update -- must reach
+    the same state bit for bit (FK_DETERMINISTIC on both sides)."""
+    X, C0 = synth.make(2, B=2, N=8192, dtype=dt)
+    T = 4
+    Xg = X.cuda()
     B, N, d = X.shape
     K = C0.shape[1]
     labels = torch.empty((B, N), dtype=torch.int32, device="cuda")
     counts = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    ws = fk.workspace(fk.problem(B, N, K, d, X.dtype, deterministic=True))
     C = C0.cuda().clone()
-    fk.fk_lloyd(X, C, labels, counts, max_iters=3)
-    torch.cuda.synchronize()
+    for t in range(T):
+        C_t = C.clone()
+        fk.fk_lloyd(Xg, C, labels, counts, max_iters=1, ws=ws, deterministic=True)
+        torch.cuda.synchronize()
+        rne = oracle.encode_rne(C_t.cpu().numpy(), dt)
+        Cq_t = torch.from_numpy(rne.view(np.int16)).view(X.dtype)
+        st = check_labels(labels, X, Cq_t)
+        su = check_update(X, labels, C_t, C, counts)
+        print(f"[lloyd {dt}] iteration {t}: labels {st} update {su}", flush=True)
     C2 = C0.cuda().clone()
-    Cq = C2.half()
     lab2 = torch.empty_like(labels)
     cnt2 = torch.empty_like(counts)
-    for _ in range(3):
-        fk.fk_assign(X, Cq, lab2)
-        Cn = torch.empty_like(C2)
-        fk.fk_update(X, lab2, C2, Cn, Cq, cnt2)
-        C2 = Cn
+    fk.fk_lloyd(Xg, C2, lab2, cnt2, max_iters=T, ws=ws, deterministic=True)
     torch.cuda.synchronize()
-    # atomics may reorder fp32 sums; near-ties aside labels agree
-    agree = (labels == lab2).float().mean().item()
-    assert agree > 0.999
-    assert (C - C2).abs().max().item() < 1e-2
+    assert torch.equal(lab2, labels)
+    assert torch.equal(cnt2, counts)
+    assert torch.equal(C2, C)
 
 
 def test_free_run_small_fp32():
