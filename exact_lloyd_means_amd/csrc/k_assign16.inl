@@ -51,6 +51,56 @@ struct Mfma16<__bf16> {
     }
 };
 
+// Direct global -> LDS loads (gfx950 global_load_lds_dword{,x4}): lane i
+// of the wave fetches base + voff and the data lands at LDS byte
+// lds + 16 i (4 i for the 4-byte form); lds must be wave-uniform.  Written
+// as inline assembly so the compiler does not order every later LDS access
+// behind the load (it cannot tell which LDS bytes the load writes); the
+// kernel waits for them itself (wait_vm).  The LDS address goes through m0,
+// which is saved and restored around the load (the load reads it at issue).
+// The loads write no vector register.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(lds), "s"(base)
+        : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const void* base, uint32_t voff, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(lds), "s"(base)
+        : "memory");
+}
+// Waits until at most N vector memory operations of this wave are in
+// flight (s_waitcnt vmcnt(N); the LDS and export counters are not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// LDS slot (16-byte unit within the row) of chunk ch of centroid row `row`
+// in a tile whose rows hold RC chunks.  gfx950's LDS has 64 four-byte banks
+// (256 bytes); a row of RC chunks covers RC of the 16 bank groups, so 16 / RC
+// consecutive rows share a 256-byte bank line.  The chunk index is XORed
+// with a function of the row that makes any 16 consecutive rows read at one
+// chunk index land in 16 different bank groups: the fragment reads (16 rows,
+// one chunk) and the staging stores (consecutive chunks) are then free of
+// bank conflicts.  (Rows padded by 16 bytes instead measured four conflict
+// cycles per fragment read.)
+template <int RC>
+__device__ __forceinline__ int lds_slot(int row, int ch) {
+    constexpr int G = RC >= 16 ? 1 : 16 / RC;  // rows per 256-byte bank line
+    constexpr int M = RC >= 16 ? 15 : RC - 1;
+    return ch ^ ((row / G) & M);
+}
+
 // S = k-steps of 32 dimensions (d <= 32 S), NP = 16-point column blocks held
 // by each wave, VEC / EXACT / SMALLK as in k_assign.  MAT: instead of the
 // running argmax, every score is written to D [B][N][K] fp32 (the distance
@@ -73,11 +123,16 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
     using MS = Mfma<T>;
     constexpr int V = 8;                               // elements per 16-byte chunk
     constexpr int RC = 4 * S;                          // 16-byte chunks per row
-    constexpr int ROWB = RC * 16 + 16;                 // LDS bytes per centroid row (padded)
+    constexpr int ROWB = RC * 16;                      // LDS bytes per centroid row
     constexpr int TILEB = kAssignBK * ROWB;
     constexpr int CHUNKS = kAssignBK * RC;             // 16-byte chunks per centroid tile
     constexpr int NT = W * kWave;
     constexpr int PER = (CHUNKS + NT - 1) / NT;
+    // Centroid tiles move global -> LDS by direct loads (no registers, no
+    // LDS store instructions) when the tile is whole 16-byte chunks that
+    // the waves cover evenly; otherwise through registers.
+    constexpr bool DMA = VEC && !SMALLK && CHUNKS % NT == 0;
+    constexpr int BIASB = DMA ? W * kWave * 4 : kAssignBK * 4;  // bias bytes per ring buffer
     constexpr int PTS = W * NP * 16;                   // points per item
     constexpr int RB = 2;                              // row blocks per tile
     constexpr int kSlots = S * RB;
@@ -88,7 +143,9 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* s_tile = smem;                                                      // [ring][TILEB]
-    float* s_bias = reinterpret_cast<float*>(smem + kAssignRing * TILEB);     // [ring][BK]
+    float* s_bias = reinterpret_cast<float*>(smem + kAssignRing * TILEB);     // [ring][BIASB]
+    const uint32_t lds_tile = (uint32_t)(uintptr_t)s_tile;
+    const uint32_t lds_bias = (uint32_t)(uintptr_t)s_bias;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -102,7 +159,7 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
     const int64_t items = B * nbpp;
 
     int crow[PER], ccol[PER];
-    uint32_t goff[PER];
+    uint32_t goff[PER], soff[PER];
     // A tile of fewer chunks than threads (d <= 32): each chunk is loaded
     // and stored by NT / CHUNKS threads (same value, same place), so no
     // thread waits behind a branch and the tile loop stays one block.
@@ -114,7 +171,23 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
         ccol[u] = c % RC;
         const int cofs = EXACT ? ccol[u] * V : min(ccol[u] * V, d - V);
         goff[u] = (uint32_t)((crow[u] * d + cofs) * (int)sizeof(T));
+        soff[u] = (uint32_t)(crow[u] * ROWB + lds_slot<RC>(crow[u], ccol[u]) * 16);
+        if constexpr (DMA) {
+            // direct load u of this wave fills LDS chunks (u W + wave) 64 + lane
+            // of the tile in order; the chunk that belongs there (the slot
+            // map is its own inverse) is the one this lane fetches
+            const int pos = (u * W + wave) * kWave + lane;
+            const int row = pos / RC, ch = lds_slot<RC>(row, pos % RC);
+            const int eofs = EXACT ? ch * V : min(ch * V, d - V);
+            goff[u] = (uint32_t)((row * d + eofs) * (int)sizeof(T));
+        }
     }
+    // LDS byte offset (within a tile, row block 0) of the fragment of k-step
+    // s this lane reads: row col, chunk 4 s + g, one register per k-step
+    uint32_t faddr[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+        faddr[s] = (uint32_t)(col * ROWB + lds_slot<RC>(col, 4 * s + g) * 16);
     auto tile_base = [&](int t) { return SMALLK ? 0 : min(t * kAssignBK, lastbase); };
     struct Staged {
         u32x4 v[PER];
@@ -168,22 +241,35 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
 #pragma unroll
             for (int u = 0; u < PER; ++u)
                 if (CHUNKS % NT == 0 || CHUNKS < NT || u * NT + tid < CHUNKS)
-                    *reinterpret_cast<u32x4*>(s_tile + buf * TILEB + crow[u] * ROWB +
-                                              ccol[u] * 16) = st.v[u];
+                    *reinterpret_cast<u32x4*>(s_tile + buf * TILEB + soff[u]) = st.v[u];
             s_bias[buf * kAssignBK + (tid & (kAssignBK - 1))] = st.bias;
         };
+        // Direct loads of tile t into LDS buffer buf: PER 16-byte loads per
+        // lane for the rows, one 4-byte load per lane for the bias (each
+        // wave fills its own copy of the 32 values, twice).
+        auto dma_tile = [&](int t, int buf) {
+            const uint32_t tb = (uint32_t)tile_base(t);
+            const uint32_t rows = tb * (uint32_t)d * (uint32_t)sizeof(T);
+#pragma unroll
+            for (int u = 0; u < PER; ++u)
+                lds_dma16(Cb, rows + goff[u],
+                          __builtin_amdgcn_readfirstlane(lds_tile + buf * TILEB + (u * W + wave) * 1024));
+            lds_dma4(biasb, (tb + (lane & (kAssignBK - 1))) * 4u,
+                     __builtin_amdgcn_readfirstlane(lds_bias + buf * BIASB + wave * kWave * 4));
+        };
         // fragment of slot sl (k-step sl / RB, row block sl % RB) of the tile
-        // in LDS buffer buf: row 16 rb + col, chunk 4 s + g
+        // in LDS buffer buf: row 16 rb + col, chunk 4 s + g (at its slot)
         auto frag = [&](int buf, int sl) -> u32x4 {
             const int s = sl / RB, rb = sl % RB;
-            return *reinterpret_cast<const u32x4*>(s_tile + buf * TILEB + (16 * rb + col) * ROWB +
-                                                   (4 * s + g) * 16);
+            return *reinterpret_cast<const u32x4*>(s_tile + buf * TILEB + rb * 16 * ROWB +
+                                                   faddr[s]);
         };
         // bias of this lane's accumulator rows 16 rb + 4 g + i
         auto bias_vec = [&](int buf, floatx4 (&bv)[RB]) {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-                bv[rb] = *reinterpret_cast<const floatx4*>(s_bias + buf * kAssignBK + 16 * rb + 4 * g);
+                bv[rb] = *reinterpret_cast<const floatx4*>(
+                    s_bias + buf * (BIASB / 4) + (DMA ? wave * kWave : 0) + 16 * rb + 4 * g);
         };
 
         // MAT: lane (g, col) holds scores of centroids 16 rb + 4 g + i
@@ -249,19 +335,25 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
         };
 
         floatx4 acc[2][RB][NP];
-        Staged st[2];
+        Staged st[DMA ? 1 : 2];
         u32x4 a[kSlots];  // centroid fragments of the tile whose MFMAs run next
         floatx4 bv[RB];   // and its bias
 
-        // ---- prologue: tiles 0, 1, 2 into LDS, tile 3 staged; tile 0's
-        // MFMAs; tile 1's first fragments and bias prefetched
-        gload(0, st[0]);
-        gload(1, st[1]);
-        sstore(0, st[0]);
-        sstore(1, st[1]);
-        gload(2, st[0]);
-        gload(3, st[1]);
-        sstore(2, st[0]);
+        // ---- prologue: tiles 0, 1, 2 into LDS (and tile 3 on its way);
+        // tile 0's MFMAs; tile 1's first fragments and bias prefetched
+        if constexpr (DMA) {
+#pragma unroll
+            for (int q = 0; q < kAssignRing; ++q) dma_tile(q, q);
+            wait_vm<PER + 1>();  // tiles 0..2 have landed
+        } else {
+            gload(0, st[0]);
+            gload(1, st[1]);
+            sstore(0, st[0]);
+            sstore(1, st[1]);
+            gload(2, st[0]);
+            gload(3, st[1]);
+            sstore(2, st[0]);
+        }
         __syncthreads();
         bias_vec(0, bv);
 #pragma unroll
@@ -275,6 +367,9 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
 #pragma unroll
         for (int q = 0; q < P; ++q) a[q] = frag(1, q);
         bias_vec(1, bv);
+        // iteration 0 reloads buffer 0 (DMA); the register path stores tile 3
+        // into buffer 3 at its end
+        if constexpr (DMA) __syncthreads();
 
         // ---- iteration t (t + 1 < ntiles), i = t mod 4 (see k_assign)
         auto iteration = [&](int t, int i) {
@@ -283,7 +378,12 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
             const int b1 = (i + 1) % kAssignRing;  // tile t+1
             const int b2 = (i + 2) % kAssignRing;  // tile t+2
             const int b3 = (i + 3) % kAssignRing;  // receives tile t+3
-            gload(t + 4, st[i & 1]);
+            // tile t + 4 replaces tile t (read for the last time before the
+            // previous barrier); it is first read two iterations later
+            if constexpr (DMA)
+                dma_tile(t + 4, i);
+            else
+                gload(t + 4, st[i & 1]);
             u32x4 nx[P];
             floatx4 nbv[RB];
             __builtin_amdgcn_sched_barrier(0);
@@ -331,7 +431,10 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) bv[rb] = nbv[rb];
             __builtin_amdgcn_s_setprio(0);
-            sstore(b3, st[(i & 1) ^ 1]);
+            if constexpr (DMA)
+                wait_vm<PER + 1>();  // tile t + 3 (issued an iteration ago) has landed
+            else
+                sstore(b3, st[(i & 1) ^ 1]);
             __syncthreads();
         };
         auto final_epilogue = [&](int t, const floatx4(&sc)[RB][NP]) {
@@ -397,7 +500,10 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
                 if (min_dist) min_dist[b * N + j] = xx - 2.f * sc;
             }
         }
-        __syncthreads();  // the next item's prologue rewrites the ring
+        // the next item's prologue rewrites the ring: no direct load of this
+        // item may still be in flight, and no wave may still be reading
+        if (DMA && item + gridDim.x < items) wait_vm<0>();
+        __syncthreads();
     }
 }
 
@@ -427,7 +533,9 @@ hipError_t launch_assign16_t(const void* X, const void* C, const float* bias, in
                              float* min_dist, int64_t B, int64_t N, int64_t K, int d,
                              hipStream_t s, float* D = nullptr, int64_t grid_wgs = 0) {
     static_assert(!MAT || W == kAssignWaves, "scores mode uses the default shape");
-    constexpr int lds = kAssignRing * (kAssignBK * (4 * S * 16 + 16) + kAssignBK * 4);
+    constexpr int RC = 4 * S, CHUNKS = kAssignBK * RC;
+    constexpr bool DMA = VEC && !SMALLK && CHUNKS % (W * kWave) == 0;
+    constexpr int lds = kAssignRing * (kAssignBK * RC * 16 + (DMA ? W * kWave * 4 : kAssignBK * 4));
     static_assert(lds <= kLdsBytes, "LDS budget");
     constexpr int PTS = W * NP * 16;
     const void* kern;
