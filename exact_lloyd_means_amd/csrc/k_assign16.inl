@@ -500,9 +500,10 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
                 if (min_dist) min_dist[b * N + j] = xx - 2.f * sc;
             }
         }
-        // the next item's prologue rewrites the ring: no direct load of this
-        // item may still be in flight, and no wave may still be reading
-        if (DMA && item + gridDim.x < items) wait_vm<0>();
+        // the next item's prologue rewrites the ring, and the workgroup's
+        // LDS is released when it ends: no direct load of this item may
+        // still be in flight, and no wave may still be reading
+        if constexpr (DMA) wait_vm<0>();
         __syncthreads();
     }
 }
