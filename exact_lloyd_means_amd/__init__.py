@@ -50,6 +50,7 @@ _SIG = {
     "fk_sort_labels": ([_PP, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "fk_update": ([_PP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "fk_update_bias": ([_PP, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "fk_update_bias_noalloc": ([_PP, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "fk_lloyd": ([_PP, _P, _P, _P, _P, ctypes.c_int, ctypes.c_float,
                   ctypes.POINTER(ctypes.c_int), _P, ctypes.c_size_t, _P], ctypes.c_int),
     "fk_lloyd_streamed": ([_PP, _P, ctypes.c_int64, _P, _P, _P, ctypes.c_int, _P, ctypes.c_size_t,
@@ -289,6 +290,21 @@ def fk_update_bias(X: torch.Tensor, labels: torch.Tensor, C_prev: torch.Tensor,
     _check(lib.fk_update_bias(ctypes.byref(p), _ptr(X), _ptr(labels), _ptr(C_prev), _ptr(C_next),
                               _ptr(C_next_lowp), _ptr(counts), _ptr(bias_next), _ptr(ws),
                               ws.numel(), _stream(stream)), "fk_update_bias")
+
+
+def fk_update_bias_noalloc(X: torch.Tensor, labels: torch.Tensor, C_prev: torch.Tensor,
+                           C_next: torch.Tensor, C_next_lowp: torch.Tensor | None,
+                           counts: torch.Tensor, bias_next: torch.Tensor, stream=None,
+                           deterministic: bool = False) -> None:
+    """fk_update_bias on the library's static per-device scratch: no
+    workspace, nothing allocated.  Calls that overlap on one GPU race."""
+    p, dev = _update_args(X, labels, C_prev, C_next, C_next_lowp, counts, deterministic)
+    _want(bias_next, "bias_next", torch.float32, (p.B, p.K), dev)
+    _need_gpu(dev)
+    _check(lib.fk_update_bias_noalloc(ctypes.byref(p), _ptr(X), _ptr(labels), _ptr(C_prev),
+                                      _ptr(C_next), _ptr(C_next_lowp), _ptr(counts),
+                                      _ptr(bias_next), _stream(stream)),
+           "fk_update_bias_noalloc")
 
 
 def _lloyd_args(X, C, labels, counts, deterministic, x_device=True):

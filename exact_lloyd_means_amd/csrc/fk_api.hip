@@ -1,9 +1,12 @@
 // fk_api.hip -- host side of the C ABI declared in include/fk.h: argument
 // checks (before anything is enqueued), workspace layout and kernel sequence
-// of each entry point.  No device memory is allocated here.
+// of each entry point.  No device memory is allocated here; the one static
+// array (the scratch of fk_update_bias_noalloc) comes with the code object.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "fk_internal.h"
 
@@ -307,9 +310,10 @@ fk_status fk_sort_labels(const fk_problem* p, const int32_t* labels, int32_t* co
 }  // extern "C"
 
 namespace {
-fk_status update_impl(const fk_problem* p, const void* X, const int32_t* labels,
-                      const float* C_prev, float* C_next, void* C_next_lowp, int32_t* counts,
-                      float* bias_next, void* ws, size_t ws_bytes, void* stream) {
+// Checks shared by the update entry points (everything but the workspace).
+fk_status check_update(const fk_problem* p, const void* X, const int32_t* labels,
+                       const float* C_prev, const float* C_next, const void* C_next_lowp,
+                       const int32_t* counts) {
     FK_CHECK(check_problem(p));
     FK_CHECK(check_ptr(X, "X"));
     FK_CHECK(check_ptr(labels, "labels"));
@@ -317,13 +321,17 @@ fk_status update_impl(const fk_problem* p, const void* X, const int32_t* labels,
     FK_CHECK(check_ptr(C_next, "C_next"));
     FK_CHECK(check_ptr(C_next_lowp, "C_next_lowp", false));
     FK_CHECK(check_ptr(counts, "counts"));
-    if (p->dtype == FK_F32 && C_next_lowp && C_next_lowp == static_cast<void*>(C_next))
+    if (p->dtype == FK_F32 && C_next_lowp && C_next_lowp == static_cast<const void*>(C_next))
         return fail(FK_EINVAL, "C_next_lowp must differ from C_next");
     if (p->d > 1024) return fail(FK_EUNSUPPORTED, "update supports d <= 1024");
     FK_CHECK(check_deterministic(*p));
-    Workspace w;
-    FK_CHECK(check_ws(*p, ws, ws_bytes, &w));
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    return FK_OK;
+}
+
+// The update's kernels (argsort, segment sums and finalize) on workspace w.
+fk_status enqueue_update(const fk_problem* p, const Workspace& w, const void* X,
+                         const int32_t* labels, const float* C_prev, float* C_next,
+                         void* C_next_lowp, int32_t* counts, float* bias_next, hipStream_t s) {
     const int64_t rows = p->B * p->K;
     FK_CHECK(enqueue_sort(*p, w, labels, counts, w.offsets, w.sorted_idx, true, nullptr, s));
     SegParams sp{true,    w.sums,  w.arrive, C_prev, C_next,
@@ -335,6 +343,56 @@ fk_status update_impl(const fk_problem* p, const void* X, const int32_t* labels,
         FK_TRY(hipMemcpyAsync(C_next_lowp, C_next, (size_t)(rows * p->d) * sizeof(float),
                               hipMemcpyDeviceToDevice, s),
                "copy fp32 centroids");
+    return FK_OK;
+}
+
+fk_status update_impl(const fk_problem* p, const void* X, const int32_t* labels,
+                      const float* C_prev, float* C_next, void* C_next_lowp, int32_t* counts,
+                      float* bias_next, void* ws, size_t ws_bytes, void* stream) {
+    FK_CHECK(check_update(p, X, labels, C_prev, C_next, C_next_lowp, counts));
+    Workspace w;
+    FK_CHECK(check_ws(*p, ws, ws_bytes, &w));
+    return enqueue_update(p, w, X, labels, C_prev, C_next, C_next_lowp, counts, bias_next,
+                          static_cast<hipStream_t>(stream));
+}
+
+// Scratch of fk_update_bias_noalloc: part of the library's code object, so
+// every GPU the library runs on holds its own copy, at its own address, from
+// the library's load on that device until the process ends.  The array's
+// name is a host-side stand-in: host code uses only the device address that
+// hipGetSymbolAddress returns for the device (scratch_address below).
+static __device__ __align__(256) unsigned char scratch[FK_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch array on the device of stream s (the
+// current device for the null stream), looked up on the first call for that
+// device with that device current and kept for the process.
+fk_status scratch_address(hipStream_t s, void** out) {
+    int cur = 0, dev = 0;
+    FK_TRY(hipGetDevice(&cur), "current device");
+    dev = cur;
+    if (s) FK_TRY(hipStreamGetDevice(s, &dev), "device of the stream");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(FK_EUNSUPPORTED, "device %d: static scratch is kept for devices 0..%d", dev,
+                    kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur) FK_TRY(hipSetDevice(dev), "select the stream's device");
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess && r != hipSuccess) return hip_fail(r, "restore the current device");
+        }
+        if (e != hipSuccess) return hip_fail(e, "address of the static scratch");
+        if (!ptr || (reinterpret_cast<uintptr_t>(ptr) & 255u))
+            return fail(FK_EHIP, "static scratch at %p is not 256-byte aligned", ptr);
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
     return FK_OK;
 }
 }  // namespace
@@ -355,6 +413,25 @@ fk_status fk_update_bias(const fk_problem* p, const void* X, const int32_t* labe
     FK_CHECK(check_ptr(bias_next, "bias_next"));
     return update_impl(p, X, labels, C_prev, C_next, C_next_lowp, counts, bias_next, ws, ws_bytes,
                        stream);
+}
+
+fk_status fk_update_bias_noalloc(const fk_problem* p, const void* X, const int32_t* labels,
+                                 const float* C_prev, float* C_next, void* C_next_lowp,
+                                 int32_t* counts, float* bias_next, void* stream) {
+    FK_CHECK(check_problem(p));
+    FK_CHECK(check_ptr(bias_next, "bias_next"));
+    FK_CHECK(check_update(p, X, labels, C_prev, C_next, C_next_lowp, counts));
+    const size_t need = workspace_layout(*p, nullptr).total;
+    if (need > (size_t)FK_NOALLOC_SCRATCH_BYTES)
+        return fail(FK_EUNSUPPORTED,
+                    "problem needs %zu bytes of scratch, the static scratch holds %zu "
+                    "(use fk_update_bias with a workspace)",
+                    need, (size_t)FK_NOALLOC_SCRATCH_BYTES);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ptr = nullptr;
+    FK_CHECK(scratch_address(s, &ptr));
+    const Workspace w = workspace_layout(*p, static_cast<char*>(ptr));
+    return enqueue_update(p, w, X, labels, C_prev, C_next, C_next_lowp, counts, bias_next, s);
 }
 
 fk_status fk_lloyd(const fk_problem* p, const void* X, float* C, int32_t* labels,

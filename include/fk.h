@@ -32,7 +32,9 @@
  *           the library allocates no device memory, keeps no pointer after a
  *           call returns and holds no state between calls (fk_last_error
  *           aside).  Scratch space comes from the caller's workspace `ws`
- *           of `ws_bytes` bytes (see fk_workspace_size).
+ *           of `ws_bytes` bytes (see fk_workspace_size); only
+ *           fk_update_bias_noalloc uses the library's static scratch
+ *           instead.
  *  Streams  `stream` is a hipStream_t passed as void*; NULL is the null
  *           stream.  All device work is enqueued asynchronously on it.
  *           Calls on different streams are safe when their workspaces and
@@ -207,6 +209,40 @@ fk_status fk_update(const fk_problem* p, const void* X, const int32_t* labels,
 fk_status fk_update_bias(const fk_problem* p, const void* X, const int32_t* labels,
                          const float* C_prev, float* C_next, void* C_next_lowp, int32_t* counts,
                          float* bias_next, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Bytes of the static scratch of fk_update_bias_noalloc, per device.
+ */
+#define FK_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * fk_update_bias_noalloc -- fk_update_bias for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments without ws and
+ * ws_bytes, the same kernels and results, and nothing allocated, by the
+ * library or by the caller.  Its scratch is one array of
+ * FK_NOALLOC_SCRATCH_BYTES bytes in the library's code object: each GPU
+ * the library runs on holds its own copy until the process ends.  The
+ * first call on a device (the device of `stream`, the current device for
+ * the null stream) looks up the array's address there; later calls reuse
+ * it.
+ *   Size     a problem whose workspace (fk_workspace_size with chunk_points
+ *            = 0) exceeds FK_NOALLOC_SCRATCH_BYTES is rejected with
+ *            FK_EUNSUPPORTED before anything is enqueued (B = 32, N = 65536,
+ *            K = 1024, d = 128 needs about 35 MiB).
+ *   Races    every call on one GPU shares that GPU's scratch: calls whose
+ *            work overlaps on one GPU (different streams, or host threads
+ *            enqueueing on different streams) race and give undefined
+ *            results.  Calls on one stream run in order and are safe.
+ *   State    the scratch keeps the last call's contents; each call clears
+ *            what it needs cleared itself (with kernels, not memsets).
+ *   Errors   as fk_update_bias, plus FK_EHIP if the scratch's address
+ *            cannot be found on the device.  fk_error_count does not apply
+ *            (there is no workspace to pass).
+ */
+fk_status fk_update_bias_noalloc(const fk_problem* p, const void* X, const int32_t* labels,
+                                 const float* C_prev, float* C_next, void* C_next_lowp,
+                                 int32_t* counts, float* bias_next, void* stream);
 
 /*
  * fk_lloyd -- max_iters Lloyd iterations (papernotes.org notes, 整体框架

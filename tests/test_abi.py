@@ -207,3 +207,42 @@ def test_workspace_bytes_zero_on_error():
     assert fk.lib.fk_workspace_bytes(ctypes.byref(p), 0) == 0
     assert b"sizes" in fk.lib.fk_last_error()
     assert fk.lib.fk_workspace_bytes(ctypes.byref(P()), -1) == 0
+
+
+def noalloc_limit():
+    m = re.search(r"#define FK_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    return int(m.group(1)) << int(m.group(2))
+
+
+def call_noalloc(p, X=FAKE, labels=FAKE, C_prev=FAKE, C_next=FAKE, lowp=None, counts=FAKE,
+                 bias=FAKE):
+    return fk.lib.fk_update_bias_noalloc(ctypes.byref(p), X, labels, C_prev, C_next, lowp,
+                                         counts, bias, None)
+
+
+def test_noalloc_scratch_holds_the_mixture_workloads():
+    limit = noalloc_limit()
+    assert limit == 64 << 20
+    for det in (0, fk.FK_DETERMINISTIC):
+        assert ws_size(P(32, 65536, 1024, 128, fk.FK_F16, det)) <= limit
+        assert ws_size(P(1, 1 << 20, 4096, 128, fk.FK_F16, det)) <= limit
+
+
+def test_noalloc_rejects_problems_beyond_the_scratch():
+    # checked before the scratch is looked up, so no GPU is needed
+    p = P(1, 1 << 24, 4096, 128)
+    assert ws_size(p) > noalloc_limit()
+    assert call_noalloc(p) == fk.FK_EUNSUPPORTED
+    assert b"static scratch" in fk.lib.fk_last_error()
+
+
+@pytest.mark.parametrize("which", ["X", "labels", "C_prev", "C_next", "counts", "bias"])
+def test_noalloc_null_and_misaligned_pointers(which):
+    assert call_noalloc(P(), **{which: None}) == fk.FK_EINVAL
+    assert call_noalloc(P(), **{which: FAKE_MISALIGNED}) == fk.FK_EINVAL
+
+
+def test_noalloc_validation():
+    assert call_noalloc(P(d=2048)) == fk.FK_EUNSUPPORTED
+    assert call_noalloc(P(dtype=fk.FK_F32), C_next=FAKE, lowp=FAKE) == fk.FK_EINVAL
+    assert call_noalloc(P(flags=4)) == fk.FK_EINVAL

@@ -118,3 +118,13 @@ def test_baselines_reject():
         fk.fk_baseline_scores(t["X"], t["Cq"], t["bias"], torch.zeros(B, N, K + 1))
     with pytest.raises(ValueError, match="labels must be torch.int32"):
         fk.fk_baseline_argmin(torch.zeros(B, N, K), torch.zeros(B, N, dtype=torch.int64))
+
+
+def test_noalloc_rejects_before_the_library():
+    t = good()
+    with pytest.raises(ValueError, match="bias_next must have shape"):
+        fk.fk_update_bias_noalloc(t["X"], t["labels"], t["C"], t["C"].clone(), t["Cq"],
+                                  t["counts"], torch.zeros(B, K + 1, dtype=torch.float32))
+    with pytest.raises(ValueError, match="on the GPU"):
+        fk.fk_update_bias_noalloc(t["X"], t["labels"], t["C"], t["C"].clone(), t["Cq"],
+                                  t["counts"], t["bias"])
