@@ -895,12 +895,15 @@ __device__ inline void finalize_row(const SegOut<T>& o, int64_t b, int64_t K, in
     }
     const float fn = (float)count;
     float cn = 0.f, mv = 0.f;
+    // the previous centroid is read only for the move (C_prev may alias
+    // C_next, so before the store)
+    const bool want_move = o.move != nullptr;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
         const int j = e0 + e;
         if (j < d) {
             const float c = s[e] / fn;
-            const float pv = EARLY ? prev[e] : o.C_prev[base + j];
+            const float pv = EARLY ? prev[e] : (want_move ? o.C_prev[base + j] : c);
             o.C_next[base + j] = c;
             float cq = c;
             if (o.lowp) {
@@ -1023,7 +1026,7 @@ __global__ __launch_bounds__(kBlock) void k_segment_sums(
             vidx[v] = sorted_idx[b * N + min((int64_t)p0 + v * kWave + lane, N - 1)];
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
-            prev[e] = FINAL && o.C_next && active && (VEC || e0 + e < d)
+            prev[e] = FINAL && o.C_next && o.move && active && (VEC || e0 + e < d)
                           ? o.C_prev[(b * K + k) * d + e0 + e]
                           : 0.f;
         s0 = __builtin_amdgcn_readfirstlane(off[k]);
@@ -1059,19 +1062,19 @@ __global__ __launch_bounds__(kBlock) void k_segment_sums(
                 else
                     v[u] = load_row_part<T, EPL, VEC>(Xb, row, d, active ? e0 : 0);
             }
+            // every loaded row is consumed on one path (a select keeps the
+            // sum of rows past n unchanged), so no load can be sunk below
+            // the waits for the others: a last row loaded only on a
+            // full-batch branch cost a whole extra round trip per batch
             if (active) {
-                if (base + RB <= n) {
 #pragma unroll
-                    for (int u = 0; u < RB; ++u)
+                for (int u = 0; u < RB; ++u) {
+                    const bool in = base + u < n;
 #pragma unroll
-                        for (int e = 0; e < EPL; ++e) acc[e] += to_f32(v[u].v[e]);
-                } else {
-#pragma unroll
-                    for (int u = 0; u < RB; ++u)
-                        if (base + u < n) {
-#pragma unroll
-                            for (int e = 0; e < EPL; ++e) acc[e] += to_f32(v[u].v[e]);
-                        }
+                    for (int e = 0; e < EPL; ++e) {
+                        const float t = acc[e] + to_f32(v[u].v[e]);
+                        acc[e] = in ? t : acc[e];
+                    }
                 }
             }
         }
