@@ -167,39 +167,9 @@ __device__ inline void clear_multi_rows(const int32_t* __restrict__ counts,
     }
 }
 
-// Exclusive scan of v[0..n) in LDS (n <= kBlock * kPlanPer), in place, by
-// one workgroup; returns the total.  Each thread owns kPlanPer consecutive
-// entries.
 constexpr int kPlanPer = 16;
 constexpr int kPlanBlock = kBlock * kPlanPer;  // labels per plan workgroup
 static_assert(kPlanBlock == kPlanLabels, "plan block size");
-__device__ inline int32_t lds_exclusive_scan(int32_t* __restrict__ v, int n,
-                                             int32_t* __restrict__ s_part) {
-    const int i0 = threadIdx.x * kPlanPer;
-    int32_t local = 0;
-#pragma unroll
-    for (int u = 0; u < kPlanPer; ++u) local += i0 + u < n ? v[i0 + u] : 0;
-    s_part[threadIdx.x] = local;
-    __syncthreads();
-    for (int o = 1; o < kBlock; o <<= 1) {
-        const int32_t t = threadIdx.x >= o ? s_part[threadIdx.x - o] : 0;
-        __syncthreads();
-        s_part[threadIdx.x] += t;
-        __syncthreads();
-    }
-    int32_t run = s_part[threadIdx.x] - local;
-#pragma unroll
-    for (int u = 0; u < kPlanPer; ++u) {
-        if (i0 + u < n) {
-            const int32_t x = v[i0 + u];
-            v[i0 + u] = run;
-            run += x;
-        }
-    }
-    const int32_t total = s_part[kBlock - 1];
-    __syncthreads();
-    return total;
-}
 
 // ---- tiled counting sort ----------------------------------------------------
 // th[b][t][k] = #{i in tile t : labels[b][i] == k}, th[b][t][K] = labels out
@@ -330,11 +300,41 @@ __global__ __launch_bounds__(kBlock) void k_plan_totals(const int32_t* __restric
     }
 }
 
+// Inclusive scan of v over the workgroup's threads in thread order (wave
+// scans by lane shifts, then the wave totals through LDS); *total receives
+// the sum over the workgroup.  Every thread of the workgroup must call it.
+__device__ inline int32_t block_inclusive_scan(int32_t v, int32_t* __restrict__ s_w,
+                                               int32_t* total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int32_t t = __shfl_up(v, o);
+        if (lane >= o) v += t;
+    }
+    if (lane == kWave - 1) s_w[w] = v;
+    __syncthreads();
+    int32_t before = 0, all = 0;
+#pragma unroll
+    for (int q = 0; q < kBlock / kWave; ++q) {
+        const int32_t t = s_w[q];
+        before += q < w ? t : 0;
+        all += t;
+    }
+    __syncthreads();  // s_w may be reused
+    *total = all;
+    return before + v;
+}
+
 // Plan, part 2: for block blk of kPlanBlock labels of problem b, the
 // offsets (exclusive scan of the counts) and first pieces, then every piece
-// of the block's segments, written in parallel over pieces (a binary search
-// over the block's first pieces finds the segment).  The last block writes
-// the totals; block 0 of problem 0 clears the move word.
+// of the block's segments.  Thread t owns the kPlanPer consecutive labels
+// kPlanPer t .. kPlanPer t + kPlanPer - 1 of the block in registers for the
+// scans (each a scan of the per-thread totals); the results go through LDS
+// so that thread t then writes labels t, t + kBlock, ...  A segment of few
+// pieces is written by the thread that holds it; the pieces of segments with many
+// (hot clusters) are listed, numbered with a second scan, and split evenly
+// over the threads (each walks a contiguous run of them).  The last block
+// writes the totals; block 0 of problem 0 clears the move word.
 __global__ __launch_bounds__(kBlock) void k_plan(const int32_t* __restrict__ counts,
                                                  const int32_t* __restrict__ part,
                                                  int32_t* __restrict__ offsets,
@@ -342,10 +342,13 @@ __global__ __launch_bounds__(kBlock) void k_plan(const int32_t* __restrict__ cou
                                                  int32_t* __restrict__ pieces,
                                                  uint32_t* __restrict__ move, int64_t K,
                                                  int64_t M) {
+    constexpr int kBigPieces = 8;  // segments with more pieces go to the shared list
+    __shared__ int32_t s_w[kBlock / kWave];
+    __shared__ int32_t s_base[2];
     __shared__ int32_t s_off[kPlanBlock];
     __shared__ int32_t s_po[kPlanBlock];
-    __shared__ int32_t s_part[kBlock];
-    __shared__ int32_t s_base[2];
+    __shared__ int32_t s_big_k[kBlock], s_big_pos[kBlock], s_big_piece[kBlock], s_big_first[kBlock + 1];
+    __shared__ int32_t s_nbig;
     const int64_t b = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
     const int64_t k0 = blk * kPlanBlock;
     const int n = (int)min((int64_t)kPlanBlock, K - k0);
@@ -354,22 +357,61 @@ __global__ __launch_bounds__(kBlock) void k_plan(const int32_t* __restrict__ cou
         for (int64_t q = 0; q < blk; ++q) acc += part[(b * nblk + q) * 2 + threadIdx.x];
         s_base[threadIdx.x] = acc;
     }
-    for (int i = threadIdx.x; i < n; i += kBlock) {
-        const int32_t v = counts[b * K + k0 + i];
-        s_off[i] = v;
-        s_po[i] = npieces_of(v);
+    if (threadIdx.x == 0) s_nbig = 0;
+    const int i0 = threadIdx.x * kPlanPer;
+    int32_t c[kPlanPer];
+    int32_t cs = 0, ps = 0;
+#pragma unroll
+    for (int u = 0; u < kPlanPer; ++u) {
+        c[u] = i0 + u < n ? counts[b * K + k0 + i0 + u] : 0;
+        cs += c[u];
+        ps += npieces_of(c[u]);
     }
-    __syncthreads();
-    const int32_t tot_c = lds_exclusive_scan(s_off, n, s_part);
-    const int32_t tot_p = lds_exclusive_scan(s_po, n, s_part);
+    // exclusive starts of this thread's labels and pieces within the block
+    int32_t tot_c, tot_p;
+    const int32_t ic = block_inclusive_scan(cs, s_w, &tot_c);
+    const int32_t ip = block_inclusive_scan(ps, s_w, &tot_p);
     const int32_t bc = s_base[0], bp = s_base[1];
     int32_t* off = offsets + b * (K + 1);
     int32_t* po = poff + b * (K + 1);
-    for (int i = threadIdx.x; i < n; i += kBlock) {
-        off[k0 + i] = bc + s_off[i];
-        po[k0 + i] = bp + s_po[i];
-    }
     int32_t* P = pieces + b * (2 * M + 1);
+    // offsets and first pieces through LDS, so the stores below go out in
+    // label order across the lanes (coalesced)
+    int32_t ro = bc + ic - cs, rp = bp + ip - ps;  // running offset and first piece
+#pragma unroll
+    for (int u = 0; u < kPlanPer; ++u) {
+        if (i0 + u < n) {
+            s_off[i0 + u] = ro;
+            s_po[i0 + u] = rp;
+            ro += c[u];
+            rp += npieces_of(c[u]);
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += kBlock) {
+        const int64_t k = k0 + i;
+        const int32_t o0 = s_off[i], p0 = s_po[i];
+        off[k] = o0;
+        po[k] = p0;
+        const int32_t pc = (i + 1 < n ? s_po[i + 1] : bp + tot_p) - p0;
+        bool mine = pc <= kBigPieces;
+        if (!mine) {
+            const int32_t at = atomicAdd(&s_nbig, 1);
+            if (at < kBlock) {
+                s_big_k[at] = (int32_t)k;
+                s_big_pos[at] = o0;
+                s_big_piece[at] = p0;
+                s_big_first[at] = pc;  // piece count until the scan below
+            } else {
+                mine = true;  // list full: write them here
+            }
+        }
+        if (mine)
+            for (int32_t q = 0; q < pc; ++q) {
+                P[1 + p0 + q] = (int32_t)k;
+                P[1 + M + p0 + q] = o0 + q * kSegRun;
+            }
+    }
     if (blk == nblk - 1) {
         if (threadIdx.x == 0) {
             off[K] = bc + tot_c;
@@ -380,37 +422,37 @@ __global__ __launch_bounds__(kBlock) void k_plan(const int32_t* __restrict__ cou
         // waiting for the count
         for (int64_t j = bp + tot_p + threadIdx.x; j < M; j += kBlock) P[1 + j] = -1;
     }
-    // pieces of this block: a segment of few pieces is written by the thread
-    // that owns it; segments of many pieces (hot clusters) are listed and
-    // written by the whole workgroup
-    __shared__ int32_t s_big[kBlock];
-    __shared__ int32_t s_nbig;
-    if (threadIdx.x == 0) s_nbig = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += kBlock) {
-        const int32_t pc = (i + 1 < n ? s_po[i + 1] : tot_p) - s_po[i];
-        if (pc > 8) {
-            const int32_t at = atomicAdd(&s_nbig, 1);
-            if (at < kBlock) {
-                s_big[at] = i;
-                continue;
-            }
-        }
-        for (int32_t q = 0; q < pc; ++q) {
-            const int64_t j = bp + s_po[i] + q;
-            P[1 + j] = (int32_t)(k0 + i);
-            P[1 + M + j] = bc + s_off[i] + q * kSegRun;
-        }
-    }
     __syncthreads();
     const int nbig = min(s_nbig, kBlock);
-    for (int r = 0; r < nbig; ++r) {
-        const int i = s_big[r];
-        const int32_t pc = (i + 1 < n ? s_po[i + 1] : tot_p) - s_po[i];
-        for (int32_t q = threadIdx.x; q < pc; q += kBlock) {
-            const int64_t j = bp + s_po[i] + q;
-            P[1 + j] = (int32_t)(k0 + i);
-            P[1 + M + j] = bc + s_off[i] + q * kSegRun;
+    if (nbig > 0) {
+        // number the listed pieces: entry r owns flat pieces
+        // s_big_first[r] .. s_big_first[r + 1] - 1
+        const int32_t mine = (int)threadIdx.x < nbig ? s_big_first[threadIdx.x] : 0;
+        int32_t tb;
+        const int32_t inc = block_inclusive_scan(mine, s_w, &tb);
+        if ((int)threadIdx.x < nbig) s_big_first[threadIdx.x] = inc - mine;
+        if (threadIdx.x == 0) s_big_first[nbig] = tb;
+        __syncthreads();
+        // thread t writes flat pieces [t tb / kBlock, (t + 1) tb / kBlock)
+        const int32_t j0 = (int32_t)((int64_t)threadIdx.x * tb / kBlock);
+        const int32_t j1 = (int32_t)((int64_t)(threadIdx.x + 1) * tb / kBlock);
+        if (j0 < j1) {
+            int lo = 0, hi = nbig - 1;  // last entry whose first piece is <= j0
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_big_first[mid] <= j0)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            int r = lo;
+            int32_t rend = s_big_first[r + 1];
+            for (int32_t j = j0; j < j1; ++j) {
+                while (j >= rend) rend = s_big_first[++r + 1];
+                const int32_t q = j - s_big_first[r];
+                P[1 + s_big_piece[r] + q] = s_big_k[r];
+                P[1 + M + s_big_piece[r] + q] = s_big_pos[r] + q * kSegRun;
+            }
         }
     }
     if (b == 0 && blk == 0 && threadIdx.x == 0 && move) *move = 0u;
