@@ -153,17 +153,26 @@ __device__ inline int32_t npieces_of(int32_t count) { return (count + kSegRun - 
 
 // Clears the sum rows and arrival counters of the segments with more than
 // one piece (the only rows the segment sums accumulate into): workgroup wg
-// of nwg takes every nwg-th group of rows, one wave per row.
+// of nwg takes every nwg-th group of rows, one wave per row.  Each wave
+// tests 64 of its rows at once (one load per lane) and clears those that
+// need it, so the tests cost one round trip, not one per row.
 __device__ inline void clear_multi_rows(const int32_t* __restrict__ counts,
                                         float* __restrict__ sums, int32_t* __restrict__ arrive,
                                         int64_t K, int64_t d, int64_t wg, int64_t nwg) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t nw = blockDim.x / kWave;
-    for (int64_t k = wg * nw + threadIdx.x / kWave; k < K; k += nwg * nw) {
-        if (counts[k] <= kSegRun) continue;
-        float* row = sums + k * d;
-        for (int64_t c = lane; c < d; c += kWave) row[c] = 0.f;
-        if (lane == 0) arrive[k] = 0;
+    const int64_t stride = nwg * nw;
+    const int64_t k0 = wg * nw + threadIdx.x / kWave;  // this wave's rows: k0 + r stride
+    for (int64_t r0 = 0; k0 + r0 * stride < K; r0 += kWave) {
+        const int64_t k = k0 + (r0 + lane) * stride;
+        uint64_t m = __ballot(k < K && counts[k] > kSegRun);
+        while (m) {
+            const int64_t kk = k0 + (r0 + __ffsll((unsigned long long)m) - 1) * stride;
+            m &= m - 1;
+            float* row = sums + kk * d;
+            for (int64_t c = lane; c < d; c += kWave) row[c] = 0.f;
+            if (lane == 0) arrive[kk] = 0;
+        }
     }
 }
 
@@ -180,18 +189,19 @@ __global__ __launch_bounds__(kBlock) void k_tile_hist(const int32_t* __restrict_
     extern __shared__ int32_t s_hist[];  // [K + 1]
     const int64_t b = blockIdx.y;
     const int64_t t = blockIdx.x;
-    for (int64_t k = threadIdx.x; k <= K; k += kBlock) s_hist[k] = 0;
-    __syncthreads();
     const int64_t i0 = t * kSortTile;
     const int64_t i1 = min(i0 + (int64_t)kSortTile, N);
     const int32_t* lab = labels + b * N;
-    // all label loads first, so they are in flight together
+    // all label loads first, so they are in flight together (and while the
+    // bins are cleared)
     int32_t a[kSortPer];
 #pragma unroll
     for (int j = 0; j < kSortPer; ++j) {
         const int64_t i = i0 + threadIdx.x + j * kBlock;
         a[j] = i < i1 ? lab[i] : 0;
     }
+    for (int64_t k = threadIdx.x; k <= K; k += kBlock) s_hist[k] = 0;
+    __syncthreads();
     int32_t bad = 0;
 #pragma unroll
     for (int j = 0; j < kSortPer; ++j) {
@@ -226,17 +236,26 @@ __global__ __launch_bounds__(kBlock) void k_tile_colscan(int32_t* __restrict__ t
     const int64_t per = (T + kColGroups - 1) / kColGroups;
     const int64_t t0 = min(g * per, T), t1 = min(t0 + per, T);
     int32_t* col = th + b * T * (K + 1) + min(k, K);
+    // both passes load kColBatch tiles at once: whole batches, then the
+    // tail as one masked batch
+    constexpr int kColBatch = 8;
     int32_t sum = 0;
     if (k <= K) {
         int64_t t = t0;
-        for (; t + 8 <= t1; t += 8) {
-            int32_t v[8];
+        for (; t + kColBatch <= t1; t += kColBatch) {
+            int32_t v[kColBatch];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = col[(t + u) * (K + 1)];
+            for (int u = 0; u < kColBatch; ++u) v[u] = col[(t + u) * (K + 1)];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) sum += v[u];
+            for (int u = 0; u < kColBatch; ++u) sum += v[u];
         }
-        for (; t < t1; ++t) sum += col[t * (K + 1)];
+        if (t < t1) {
+            int32_t v[kColBatch];
+#pragma unroll
+            for (int u = 0; u < kColBatch; ++u) v[u] = t + u < t1 ? col[(t + u) * (K + 1)] : 0;
+#pragma unroll
+            for (int u = 0; u < kColBatch; ++u) sum += v[u];
+        }
     }
     s_tot[g][lane] = sum;
     __syncthreads();
@@ -248,20 +267,25 @@ __global__ __launch_bounds__(kBlock) void k_tile_colscan(int32_t* __restrict__ t
     }
     if (k > K) return;
     int64_t t = t0;
-    for (; t + 8 <= t1; t += 8) {
-        int32_t v[8];
+    for (; t + kColBatch <= t1; t += kColBatch) {
+        int32_t v[kColBatch];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = col[(t + u) * (K + 1)];
+        for (int u = 0; u < kColBatch; ++u) v[u] = col[(t + u) * (K + 1)];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < kColBatch; ++u) {
             col[(t + u) * (K + 1)] = run;
             run += v[u];
         }
     }
-    for (; t < t1; ++t) {
-        const int32_t v = col[t * (K + 1)];
-        col[t * (K + 1)] = run;
-        run += v;
+    if (t < t1) {
+        int32_t v[kColBatch];
+#pragma unroll
+        for (int u = 0; u < kColBatch; ++u) v[u] = t + u < t1 ? col[(t + u) * (K + 1)] : 0;
+#pragma unroll
+        for (int u = 0; u < kColBatch; ++u) {
+            if (t + u < t1) col[(t + u) * (K + 1)] = run;
+            run += v[u];
+        }
     }
     if (g == 0) {
         if (k < K)
@@ -562,15 +586,8 @@ __global__ __launch_bounds__(NW * kWave) void k_tile_scatter_w(
         b = blockIdx.y;
         t = blockIdx.x;
     }
-    if (sums) clear_multi_rows(counts + b * K, sums + b * K * d, arrive + b * K, K, d, t, T);
     const int32_t* pre = th + (b * T + t) * (K + 1);
     const int32_t* off = offsets + b * (K + 1);
-    for (int64_t k = threadIdx.x; k < K; k += NW * kWave) {
-        s_base[k] = off[k] + pre[k];
-#pragma unroll
-        for (int j = 0; j < NW / 2; ++j) s_cur[j * K + k] = 0u;
-    }
-    __syncthreads();
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t w0 = t * kSortTile + (int64_t)wave * kRange;
@@ -579,25 +596,52 @@ __global__ __launch_bounds__(NW * kWave) void k_tile_scatter_w(
     int32_t* out = sorted_idx + b * N;
     uint32_t* cur = s_cur + (wave >> 1) * K;
     const uint32_t sh = 16u * (uint32_t)(wave & 1);
+    // every global load first, so they share one round trip: this wave's
+    // labels, the bases of the labels this thread initialises, and the
+    // counts the row clearing tests
     int32_t a[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const int64_t i = w0 + j * kWave + lane;
         a[j] = i < i1 ? lab[i] : -1;
     }
+    constexpr int kBasesPer = (int)((kWaveBinsMax + NW * kWave - 1) / (NW * kWave));
+    int32_t base[kBasesPer];
+#pragma unroll
+    for (int q = 0; q < kBasesPer; ++q) {
+        const int64_t k = threadIdx.x + (int64_t)q * NW * kWave;
+        const int64_t kc = min(k, K - 1);  // unconditional loads: no wait per label
+        const int32_t v = off[kc] + pre[kc];
+        base[q] = k < K ? v : 0;
+    }
+    if (sums) clear_multi_rows(counts + b * K, sums + b * K * d, arrive + b * K, K, d, t, T);
+#pragma unroll
+    for (int q = 0; q < kBasesPer; ++q) {
+        const int64_t k = threadIdx.x + (int64_t)q * NW * kWave;
+        if (k < K) {
+            s_base[k] = base[q];
+#pragma unroll
+            for (int j = 0; j < NW / 2; ++j) s_cur[j * K + k] = 0u;
+        }
+    }
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
         if (a[j] >= 0 && a[j] < K) atomicAdd(&cur[a[j]], 1u << sh);
     __syncthreads();
     // counts -> exclusive prefixes over the waves, in wave order
+    // (all words of a label read before any is rewritten: one LDS round
+    // trip instead of one per word)
     for (int64_t k = threadIdx.x; k < K; k += NW * kWave) {
+        uint32_t c[NW / 2];
+#pragma unroll
+        for (int j = 0; j < NW / 2; ++j) c[j] = s_cur[j * K + k];
         uint32_t run = 0;
 #pragma unroll
         for (int j = 0; j < NW / 2; ++j) {
-            const uint32_t c = s_cur[j * K + k];
-            const uint32_t lo = c & 0xffffu;
+            const uint32_t lo = c[j] & 0xffffu;
             s_cur[j * K + k] = run | ((run + lo) << 16);
-            run += lo + (c >> 16);
+            run += lo + (c[j] >> 16);
         }
     }
     __syncthreads();
