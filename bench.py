@@ -127,7 +127,7 @@ def main() -> int:
     ap.add_argument("--chunk", type=int, default=1 << 24,
                     help="workload 5 only: points per streamed chunk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=25.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--groups", type=int, default=1,
                     help="split the B problems into this many groups, each on its own stream, "
@@ -290,6 +290,8 @@ def main() -> int:
     value = args.steps / (total_ms * 1e-3)
     src_hash = assign_sources_hash()
 
+    trace = objective_trace(fk, X, C0, fmt, w.iters)
+
     base = None
     if not args.no_baselines:
         base = run_baselines(X, Cq, C, labels, fmt, a_mean * G, u_mean * G)
@@ -338,6 +340,7 @@ def main() -> int:
         },
         "cpu_baseline": cpu,
         "unfused_baselines": base,
+        "iterations": trace,
     }
     if pages_ms:
         out["baseline_context"] = f"pages: {pages_ms} ms/iter on NVIDIA H200 (FP16), not this machine"
@@ -401,9 +404,9 @@ def run_sweep(args) -> int:
         shapes = [((np_, w, 0), variant(np_, w)) for np_, w in itertools.product((1, 2, 4, 8),
                                                                                    (4, 8))]
         # the shape fk_assign's dispatch picks (assign16_np and assign16_waves
-        # in k_assign16.inl: four blocks and four waves for d <= 128, two
-        # blocks and eight waves for d = 256), one workgroup per block
-        lib_shape = (4, 4, 0) if d <= 128 else (2, 8, 0)
+        # in k_assign16.inl: four blocks and four waves for d <= 256), one
+        # workgroup per block
+        lib_shape = (4, 4, 0)
         med = median_times(shapes)
         best = min(shapes, key=lambda c: med[c])
         # second round: grid caps of the best shape, timed together with the
@@ -620,11 +623,60 @@ def run_streamed(args, w) -> int:
     return 0
 
 
+def objective_trace(fk, X, C0, fmt, T):
+    """The workload's T iterations from its initial centroids, outside the
+    timed region, with the same calls as a step plus min_dist: per iteration
+    the objective sum_i |x_i - c_(a_i)|^2 (min_dist summed in fp64) of the
+    assignment and the largest cluster count of the update that follows."""
+    import torch
+
+    B, N, d = X.shape
+    K = C0.shape[1]
+    C = C0.cuda().clone()
+    Cq = C.to(X.dtype).contiguous() if fmt != "f32" else C.clone()
+    bias = torch.empty((B, K), dtype=torch.float32, device="cuda")
+    labels = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    counts = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    md = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    ws = fk.workspace(fk.problem(B, N, K, d, X.dtype))
+    fk.fk_centroid_bias(Cq, bias)
+    obj, maxc = [], []
+    for _ in range(T):
+        fk.fk_assign_with_bias(X, Cq, bias, labels, md)
+        obj.append(md.sum(dtype=torch.float64))
+        fk.fk_update_bias(X, labels, C, C, Cq if fmt != "f32" else None, counts, bias, ws=ws)
+        if fmt == "f32":
+            Cq.copy_(C)
+        maxc.append(counts.max())
+    torch.cuda.synchronize()
+    obj = [float(v) for v in obj]
+    return {
+        "objective": [float(f"{v:.9g}") for v in obj],
+        "objective_non_increasing": all(b <= a * (1 + 1e-6) for a, b in zip(obj, obj[1:])),
+        "max_cluster_count": [int(v) for v in maxc],
+        "note": "objective = sum of min_dist (fp32 per point, summed in fp64) of each "
+                "iteration's assignment; max_cluster_count of the update after it",
+    }
+
+
+def host_cpu_model() -> str:
+    """The host CPU's model name (as lscpu prints it), from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def run_cpu_baseline(w, X_cpu, Cq, fmt, target_s, gpu_value):
     import numpy as np
     import torch
 
     import oracle
+    import synth
 
     def storage(t):
         t = t.detach().contiguous().cpu()
@@ -634,38 +686,66 @@ def run_cpu_baseline(w, X_cpu, Cq, fmt, target_s, gpu_value):
 
     Xs, Cs = storage(X_cpu), storage(Cq)
     B, N, d = Xs.shape
+    K = Cs.shape[1]
     total = B * N
     rng = np.random.Generator(np.random.PCG64(7))
     threads = oracle.max_threads()
-    # probe, then size the sample for about target_s of assign work
-    probe = rng.choice(total, size=min(total, 256), replace=False)
+    # probe, then take every point if that fits about target_s of assign
+    # work, else a seeded sample
+    probe = rng.choice(total, size=min(total, 4096), replace=False)
     t = time.perf_counter()
     oracle.assign(Xs, Cs, fmt_x=fmt, fmt_c=fmt, rows=probe)
     per_row = (time.perf_counter() - t) / probe.size
     S = int(min(total, max(256, target_s / max(per_row, 1e-9))))
-    rows = rng.choice(total, size=S, replace=False)
+    rows = np.arange(total) if S == total else rng.choice(total, size=S, replace=False)
     log(f"[bench] cpu baseline: oracle assign on {S} of {total} points, {threads} threads")
     t = time.perf_counter()
-    lab, _, _ = oracle.assign(Xs, Cs, fmt_x=fmt, fmt_c=fmt, rows=rows)
+    lab, d1, d2 = oracle.assign(Xs, Cs, fmt_x=fmt, fmt_c=fmt, rows=rows)
     t_assign = (time.perf_counter() - t) * total / S
-    # update of one problem (at most its first 2^22 points), scaled linearly
+    # near ties of this assignment (gap (d2 - d1) / d2 below the parity
+    # tolerance: excluded from the bit-exact label rule)
+    tau = 1e-4 if fmt == "f32" else 1e-2
+    gap = np.where(d2 > 0, (d2 - d1) / np.where(d2 > 0, d2, 1.0), 0.0)
+    near = float(np.mean(gap < tau))
+    # update of one problem (at most its first 2^22 points), scaled
+    # linearly: on the oracle's own labels of those points when it assigned
+    # every point, else on round-robin labels (the oracle's assignment of a
+    # whole problem would take hours there; the update's cost does not
+    # depend on which labels it gets)
     Nu = min(N, 1 << 22)
-    lab0 = np.zeros((1, Nu), np.int32)
-    lab0[0, :] = np.arange(Nu) % Cs.shape[1]
+    if S == total:
+        lab0 = lab[:Nu].reshape(1, Nu).astype(np.int32)
+        upd_labels = "the oracle's labels"
+    else:
+        lab0 = (np.arange(Nu) % K).reshape(1, Nu).astype(np.int32)
+        upd_labels = "round-robin labels"
     t = time.perf_counter()
-    oracle.update(np.ascontiguousarray(Xs[:1, :Nu]), lab0, np.zeros((1, Cs.shape[1], d), np.float32),
+    oracle.update(np.ascontiguousarray(Xs[:1, :Nu]), lab0, np.zeros((1, K, d), np.float32),
                   fmt_x=fmt, fmt_c="f32")
     t_update = (time.perf_counter() - t) * B * N / Nu
     it_s = 1.0 / (t_assign + t_update)
+    # one lock-step oracle iteration of the smallest workload on one thread
+    X1, C1 = synth.make(1)
+    X1s, C1s = storage(X1), storage(C1)
+    t = time.perf_counter()
+    lab1, _, _ = oracle.assign(X1s, C1s, fmt_x="f32", fmt_c="f32", nthreads=1)
+    oracle.update(X1s, lab1, C1s, fmt_x="f32", fmt_c="f32", nthreads=1)
+    t1 = time.perf_counter() - t
+    extrap = "all points" if S == total else f"{S} random points of {total} (x{total / S:.1f} " \
+                                             "extrapolated, linear in points)"
     return {
         "value": it_s,
         "unit": "Lloyd it/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"fp64 oracle assign on {S} random points of {total} (x{total / S:.1f} "
-                   f"extrapolated, linear in points) + update of {Nu} points of 1 of {B} problems "
-                   f"(x{B * N / Nu:g}); "
+        "sample": (f"fp64 oracle assign on {extrap} + update of {Nu} points of 1 of {B} problems "
+                   f"on {upd_labels} (x{B * N / Nu:g}); "
                    f"{t_assign:.1f} s assign + {t_update:.2f} s update per iteration"),
+        "host_cpu": host_cpu_model(),
+        "near_tie_excluded_frac": round(near, 6),
+        "near_tie_note": f"points with (d2 - d1) / d2 < {tau:g} in the oracle's assignment of "
+                         "the sampled points to the centroids after the timed steps",
+        "gmm32_n4096_k32_d128_f32_single_thread_s": round(t1, 4),
         "gpu_over_cpu": round(gpu_value / it_s, 1),
     }
 
@@ -791,6 +871,40 @@ def summarize(argv) -> int:
         print("\n| counter | mean per dispatch |\n|---|---|")
         for k in sorted(mean):
             print(f"| {k} | {mean[k]:.0f} |")
+        return 0
+    if kind == "sweep":
+        # the --sweep-assign JSON line as the shape table kept in profiles/
+        path, cmd = argv[1], " ".join(argv[2:])
+        with open(path) as f:
+            rec = json.loads([ln for ln in f if ln.strip()][-1])
+        print("# fp16 assign kernel: every shape vs the library's shape rule\n")
+        print(f"command: `{cmd}` (on the GPU; medians of 7 rotating rounds of 5 launches per "
+              "shape)\n")
+        print("Workload: synth gmm1024 mixture, B=32, N=65536, K=1024, fp16, d = 64 / 128 / 256. "
+              "Shapes: point blocks per wave (NP) x waves per workgroup (W), one workgroup per "
+              "block of points; then a second rotation with grid caps (workgroups looping over "
+              "several blocks) of the best shape, timed together with the uncapped best shape and "
+              "the library's shape (their rows carry the second rotation's medians, so the "
+              "library-vs-best comparison comes from one rotation). Every shape's labels were "
+              "compared with the library's.")
+        for pd in rec["per_d"]:
+            d, lib = pd["d"], pd["library_shape"]
+            print(f"\n## d = {d}\n\n| NP | W | grid | ms | TFLOP/s | labels identical |\n"
+                  "|---|---|---|---|---|---|")
+            for r in rec["rows"]:
+                if r["d"] != d:
+                    continue
+                grid = "one per block" if r["grid_wgs"] == 0 else str(r["grid_wgs"])
+                if (r["point_blocks"], r["waves"], r["grid_wgs"]) == \
+                        (lib["point_blocks"], lib["waves"], 0):
+                    grid += " (library)"
+                print(f"| {r['point_blocks']} | {r['waves']} | {grid} | {r['ms']} | "
+                      f"{r['TFLOPs']} | {r['labels_identical']} |")
+            b = pd["best"]
+            bg = "one per block" if b["grid_wgs"] == 0 else str(b["grid_wgs"])
+            print(f"\nlibrary shape NP={lib['point_blocks']} W={lib['waves']}: "
+                  f"{pd['library_choice_ms']} ms; best NP={b['point_blocks']} W={b['waves']} "
+                  f"grid={bg}: {b['ms']} ms; library loss {pd['library_loss_pct']} %")
         return 0
     log(f"unknown summary kind {kind!r}")
     return 2

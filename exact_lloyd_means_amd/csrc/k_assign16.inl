@@ -569,23 +569,28 @@ constexpr int assign16_vgprs(int S, int NP) {
     return 4 * S * NP + 16 * NP + 8 * S + 8 * NP + 40;
 }
 
-// Point blocks per wave: the most (a power of two up to 8) whose estimate
-// fits the 256 VGPRs a lane has at two waves per SIMD.  Each centroid
-// fragment read from LDS feeds NP matrix instructions, so more is better
-// until registers spill.  Gives 4 for S <= 4 and 2 for S = 8.
+// Point blocks per wave: the most, up to four, whose register estimate
+// stays within 1.3 times the 256 VGPRs a lane has at two waves per SIMD.
+// Each centroid fragment read from LDS feeds NP matrix instructions, so
+// more is better until spilling dominates: a moderate overflow spills
+// loop-invariant point fragments to scratch (cached), which costs less than
+// halving the matrix work per fragment, while eight blocks overflow by far.
+// Measured on B=32, N=65536, K=1024 fp16 (every shape, same process): at
+// d = 256 four blocks spill 129 registers and run 10 % faster than two,
+// which fit; eight blocks spill 550-700 registers at d = 64-256 and run
+// level with four at d = 64, 4x and 6x slower at d = 128 and 256.  Gives
+// 4 for every S <= 8.
 constexpr int assign16_np(int S) {
-    return assign16_vgprs(S, 8) <= 256   ? 8
-           : assign16_vgprs(S, 4) <= 256 ? 4
-           : assign16_vgprs(S, 2) <= 256 ? 2
-                                         : 1;
+    return assign16_vgprs(S, 4) * 10 <= 256 * 13   ? 4
+           : assign16_vgprs(S, 2) * 10 <= 256 * 13 ? 2
+                                                   : 1;
 }
 
-// Waves per workgroup: four (two workgroups per CU, each with its own LDS
-// ring, so one workgroup's barrier waits overlap the other's matrix work)
-// while a workgroup still stages each centroid tile for at least 256
-// points; otherwise eight (one workgroup per CU).  Gives 4 for S <= 4 and
-// 8 for S = 8.
-constexpr int assign16_waves(int S) { return 4 * assign16_np(S) * 16 >= 256 ? 4 : 8; }
+// Waves per workgroup: four, so two workgroups share a CU, each with its
+// own LDS ring, and one workgroup's barrier waits overlap the other's
+// matrix work (eight waves, one workgroup per CU, measured 8-28 % slower
+// with four point blocks at d = 64, 128 and 256).
+constexpr int assign16_waves(int) { return 4; }
 
 // 16-bit inputs with d <= 256: S = k-steps of 32 (a power of two covering
 // d), assign16_np(S) 16-point blocks per wave, assign16_waves(S) waves.
@@ -648,9 +653,9 @@ hipError_t dispatch_scores16(const void* X, const void* C, const float* bias, fl
 }
 
 static_assert(assign16_np(1) == 4 && assign16_np(2) == 4 && assign16_np(4) == 4 &&
-                  assign16_np(8) == 2,
+                  assign16_np(8) == 4,
               "point blocks per wave");
-static_assert(assign16_waves(4) == 4 && assign16_waves(8) == 8, "waves per workgroup");
+static_assert(assign16_waves(4) == 4 && assign16_waves(8) == 4, "waves per workgroup");
 
 }  // namespace
 }  // namespace fk
