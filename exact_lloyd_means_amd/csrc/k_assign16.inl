@@ -51,40 +51,6 @@ struct Mfma16<__bf16> {
     }
 };
 
-// Direct global -> LDS loads (gfx950 global_load_lds_dword{,x4}): lane i
-// of the wave fetches base + voff and the data lands at LDS byte
-// lds + 16 i (4 i for the 4-byte form); lds must be wave-uniform.  Written
-// as inline assembly so the compiler does not order every later LDS access
-// behind the load (it cannot tell which LDS bytes the load writes); the
-// kernel waits for them itself (wait_vm).  The LDS address goes through m0,
-// which is saved and restored around the load (the load reads it at issue).
-// The loads write no vector register.
-__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, %3\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(voff), "s"(lds), "s"(base)
-        : "memory");
-}
-__device__ __forceinline__ void lds_dma4(const void* base, uint32_t voff, uint32_t lds) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, %3\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(voff), "s"(lds), "s"(base)
-        : "memory");
-}
-// Waits until at most N vector memory operations of this wave are in
-// flight (s_waitcnt vmcnt(N); the LDS and export counters are not waited on).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // LDS slot (16-byte unit within the row) of chunk ch of centroid row `row`
 // in a tile whose rows hold RC chunks.  gfx950's LDS has 64 four-byte banks
 // (256 bytes); a row of RC chunks covers RC of the 16 bank groups, so 16 / RC

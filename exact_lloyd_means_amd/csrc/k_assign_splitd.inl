@@ -38,11 +38,19 @@ constexpr int kSdStage = (kSdP + kSdK) * kSdRowB;  // LDS bytes per stage (X chu
 __device__ inline int sd_slot(int r, int s) { return r * kSdRowB + ((s ^ (r & 7)) << 4); }
 
 // VEC: d is a multiple of the 16-byte slot (slots load whole); else per element.
-template <typename T, bool VEC, bool SMALLK>
+// DMA (whole 128-byte chunks, K >= 256, each problem's rows under 4 GiB):
+// the chunks reach LDS by direct global-to-LDS loads instead of through
+// registers.  Wave w's load u fills LDS bytes [(8 u + w) KiB, +1 KiB) of the
+// stage: rows 8 (8 u + w) .. + 7, lane i taking physical slot i % 8 of row
+// (8 u + w) 8 + i / 8, i.e. the row's logical slot (i % 8) ^ (row % 8), so
+// the swizzled layout the fragment reads expect comes out of the linear
+// lane-order writes of the load.
+template <typename T, bool VEC, bool SMALLK, bool DMA>
 __global__ __launch_bounds__(kSdWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_assign_splitd(const T* __restrict__ X, const T* __restrict__ C,
                      const float* __restrict__ bias, int32_t* __restrict__ labels,
                      float* __restrict__ min_dist, int64_t N, int64_t K, int d) {
+    static_assert(!DMA || (VEC && !SMALLK), "direct loads need whole slots and full tiles");
     using M = Mfma<T>;
     constexpr int V = 16 / sizeof(T);         // elements per slot
     constexpr int EC = kSdRowB / sizeof(T);   // elements per row chunk
@@ -91,6 +99,31 @@ void k_assign_splitd(const T* __restrict__ X, const T* __restrict__ C,
         *reinterpret_cast<u32x4*>(s_stage + buf * kSdStage + sd_slot(g / kSdSlots, g % kSdSlots)) =
             v;
     };
+    // direct loads: per lane, the row and the byte offset of its logical
+    // slot inside a chunk; loads u < LPT / 2 fill point rows, the others
+    // centroid rows (kSdP / 8 / kSdWaves = LPT / 2)
+    static_assert(kSdP == kSdK && LPT == 8 && kSdSlots == 8, "direct-load layout");
+    const uint32_t rowb = (uint32_t)d * (uint32_t)sizeof(T);
+    uint32_t dma_row[LPT];  // point row (global) or centroid row within the tile
+    const uint32_t dma_slot = (uint32_t)(((lane & 7) ^ ((lane >> 3) & 7)) * 16);  // (row % 8) = lane / 8 % 8
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+        const int r = (u * kSdWaves + wave) * 8 + (lane >> 3);
+        dma_row[u] = r < kSdP ? (uint32_t)min((int)p0 + r, N32 - 1) : (uint32_t)(r - kSdP);
+    }
+    auto dma_chunk = [&](int kbase, int ch, int buf) {
+        const uint32_t cho = (uint32_t)ch * kSdRowB + dma_slot;
+        char* st = s_stage + buf * kSdStage;
+#pragma unroll
+        for (int u = 0; u < LPT; ++u) {
+            const uint32_t lds = (uint32_t)(uintptr_t)(st + (u * kSdWaves + wave) * 1024);
+            if (u < LPT / 2)
+                lds_dma16(Xb, dma_row[u] * rowb + cho, __builtin_amdgcn_readfirstlane(lds));
+            else
+                lds_dma16(Cb, ((uint32_t)kbase + dma_row[u]) * rowb + cho,
+                          __builtin_amdgcn_readfirstlane(lds));
+        }
+    };
 
     float best[4];
     int32_t bidx[4];
@@ -111,10 +144,15 @@ void k_assign_splitd(const T* __restrict__ X, const T* __restrict__ C,
             s_bias[tid] = k < K32 ? biasb[min(k, K32 - 1)] : -INFINITY;
         }
         floatx16 acc[2][4];
+        if constexpr (DMA) {
+            dma_chunk(kbase, 0, 0);
+            wait_vm<0>();
+        } else {
 #pragma unroll
-        for (int u = 0; u < LPT; ++u) pre[u] = load_slot(u, kbase, 0);
+            for (int u = 0; u < LPT; ++u) pre[u] = load_slot(u, kbase, 0);
 #pragma unroll
-        for (int u = 0; u < LPT; ++u) store_slot(u, 0, pre[u]);
+            for (int u = 0; u < LPT; ++u) store_slot(u, 0, pre[u]);
+        }
         __syncthreads();
         // bias vectors of this wave's two row blocks
         floatx16 bv[2];
@@ -134,8 +172,13 @@ void k_assign_splitd(const T* __restrict__ X, const T* __restrict__ C,
             const int buf = ch & 1;
             const bool more = ch + 1 < nch;
             if (more) {
+                // the other buffer was last read before the previous barrier
+                if constexpr (DMA) {
+                    dma_chunk(kbase, ch + 1, buf ^ 1);
+                } else {
 #pragma unroll
-                for (int u = 0; u < LPT; ++u) pre[u] = load_slot(u, kbase, ch + 1);
+                    for (int u = 0; u < LPT; ++u) pre[u] = load_slot(u, kbase, ch + 1);
+                }
             }
             // 16-bit: raised issue priority for the chunk's matrix part,
             // normal for the staging stores and the barrier (2 % faster at
@@ -163,8 +206,12 @@ void k_assign_splitd(const T* __restrict__ X, const T* __restrict__ C,
             }
             if constexpr (sizeof(T) == 2) __builtin_amdgcn_s_setprio(0);
             if (more) {
+                if constexpr (DMA) {
+                    wait_vm<0>();  // this wave's part of the next chunk has landed
+                } else {
 #pragma unroll
-                for (int u = 0; u < LPT; ++u) store_slot(u, buf ^ 1, pre[u]);
+                    for (int u = 0; u < LPT; ++u) store_slot(u, buf ^ 1, pre[u]);
+                }
             }
             __syncthreads();
         }
@@ -234,12 +281,17 @@ hipError_t launch_assign_splitd(const void* X, const void* C, const float* bias,
     constexpr size_t lds = splitd_lds();
     static_assert(lds <= 160 * 1024, "LDS budget");
     constexpr int V = 16 / sizeof(T);
-    const int variant = (K < kSdK ? 1 : 0) + (d % V == 0 ? 2 : 0);
+    constexpr int EC = kSdRowB / sizeof(T);  // elements per row chunk
+    // direct loads: whole chunks, full tiles, 32-bit byte offsets per problem
+    const bool dma = d % EC == 0 && K >= kSdK && N * (int64_t)d * (int64_t)sizeof(T) < ((int64_t)1 << 32) &&
+                     K * (int64_t)d * (int64_t)sizeof(T) < ((int64_t)1 << 32);
+    const int variant = dma ? 4 : (K < kSdK ? 1 : 0) + (d % V == 0 ? 2 : 0);
     using Kern = void (*)(const T*, const T*, const float*, int32_t*, float*, int64_t, int64_t, int);
-    const Kern kerns[4] = {k_assign_splitd<T, false, false>, k_assign_splitd<T, false, true>,
-                           k_assign_splitd<T, true, false>, k_assign_splitd<T, true, true>};
+    const Kern kerns[5] = {k_assign_splitd<T, false, false, false>, k_assign_splitd<T, false, true, false>,
+                           k_assign_splitd<T, true, false, false>, k_assign_splitd<T, true, true, false>,
+                           k_assign_splitd<T, true, false, true>};
     const Kern kern = kerns[variant];
-    static LdsAttr attr[4];
+    static LdsAttr attr[5];
     hipError_t e = ensure_lds(attr[variant], reinterpret_cast<const void*>(kern), (int)lds);
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)((N + kSdP - 1) / kSdP), (unsigned)B);
