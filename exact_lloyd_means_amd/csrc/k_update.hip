@@ -1105,11 +1105,13 @@ __global__ __launch_bounds__(kBlock) void k_segment_sums(
     int32_t s0, s1;
     int n;  // rows of this piece
     if constexpr (EARLY) {
-        // positions past the piece read whatever index follows (clamped to
-        // the array); never used
+        // positions past the piece read the index that follows, up to the
+        // last sorted one (past it the array holds no point index when
+        // labels were skipped); never added
+        const int32_t last = __builtin_amdgcn_readfirstlane(off[K]) - 1;
 #pragma unroll
         for (int v = 0; v < NV; ++v)
-            vidx[v] = sorted_idx[b * N + min((int64_t)p0 + v * kWave + lane, N - 1)];
+            vidx[v] = sorted_idx[b * N + min(p0 + v * kWave + lane, last)];
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
             prev[e] = FINAL && o.C_next && o.move && active && (VEC || e0 + e < d)
