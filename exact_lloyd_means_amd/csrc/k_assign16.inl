@@ -75,10 +75,11 @@ __device__ __forceinline__ int lds_slot(int row, int ch) {
 // Tile of 32 centroids = 2 row blocks of 16.  A slot is the NP MFMAs that
 // share one centroid fragment (row block rb, k-step s), slot order s-major;
 // in each slot every MFMA is followed by the epilogue of one row of tile t
-// for its point block (rows spread evenly over the slots).  Staging
-// (registers -> ring of four LDS buffers), the
-// prefetch of the next tile's fragments and bias, and the branch-free
-// overlapping last tile are those of k_assign.
+// for its point block (rows spread evenly over the slots).  The ring of
+// four LDS buffers, the prefetch of the next tile's fragments and bias, and
+// the branch-free overlapping last tile are those of k_assign; the tiles
+// reach the ring by direct global-to-LDS loads when every thread moves whole
+// 16-byte chunks (DMA below), else through registers as in k_assign.
 template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK, bool MAT, int W>
 __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* __restrict__ C,
                                               const float* __restrict__ bias,
@@ -354,7 +355,8 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
             floatx4 nbv[RB];
             __builtin_amdgcn_sched_barrier(0);
             // Higher issue priority for the matrix and epilogue part of the
-            // tile, back to normal for the staging stores and the barrier:
+            // tile, back to normal for the staging (stores or the wait for
+            // the direct loads) and the barrier:
             // when both waves of a SIMD are ready, the one feeding the
             // matrix unit goes first (1-4 % faster on the B=32, K=1024
             // workloads, 1-2 % of it from the ILP-first scheduler the build
