@@ -129,6 +129,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=25.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--stage-every", type=int, default=5,
+                    help="record the stage markers on every M-th timed step only")
     ap.add_argument("--groups", type=int, default=1,
                     help="split the B problems into this many groups, each on its own stream, "
                          "so one group's update can overlap another's assign")
@@ -205,10 +207,7 @@ def main() -> int:
 
     def step(g, e=None):
         """One Lloyd iteration of group g.  e: timing events recorded before
-        and after the assign (and, with several groups, after the update).
-        With one group the update of this step ends where the next step's
-        first event (or the closing event) is recorded, so a step adds only
-        two markers to the stream."""
+        and after the assign and after the update (marked steps only)."""
         sl = grp[g]
         with torch.cuda.stream(streams[g]):
             if G > 1 and args.schedule == "chain" and last[0] is not None:
@@ -225,7 +224,7 @@ def main() -> int:
             # the next assign
             fk.fk_update_bias(X[sl], labels[sl], C[sl], C[sl], Cq[sl] if fmt != "f32" else None,
                               counts[sl], bias[sl], ws=ws[g])
-            if e and G > 1:
+            if e:
                 e[2].record()
 
     log(f"[bench] {G} stream group(s) of {Hg} problems ({args.schedule}); "
@@ -235,11 +234,15 @@ def main() -> int:
             step(g)
     torch.cuda.synchronize()
 
-    # per-step markers without the system-scope fence; the closing events
-    # (start/end, for the whole-job rate) are ordinary ones
-    evs = [[[MarkerEvent() for _ in range(2 if G == 1 else 3)] for _ in range(G)]
-           for _ in range(args.steps)]
-    tail = [MarkerEvent() for _ in range(G)]
+    # stage markers (without the system-scope fence) on every
+    # --stage-every-th timed step: each marker idles the stream for a few
+    # microseconds, so marking every step would slow the timed run itself;
+    # the closing events (start/end, for the whole-job rate) are ordinary ones
+    M = max(1, args.stage_every)
+    marked = [s_ % M == M - 1 or (s_ == args.steps - 1 and args.steps < M)
+              for s_ in range(args.steps)]
+    evs = [[[MarkerEvent() for _ in range(3)] for _ in range(G)] if marked[s_] else None
+           for s_ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     log(f"[bench] timing {args.steps} steps")
@@ -251,21 +254,15 @@ def main() -> int:
         st.wait_event(start)
     for s_ in range(args.steps):
         for g in range(G):
-            step(g, evs[s_][g])
-    for g, st in enumerate(streams):
-        tail[g].record(st)
+            step(g, evs[s_][g] if evs[s_] else None)
+    for st in streams:
         main_stream.wait_stream(st)
     end.record(main_stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
-    assign_ms = [e[0].elapsed_time(e[1]) for row in evs for e in row]
-    # update of step s, group g: from its assign's end to the next step's
-    # start on the same stream
-    update_ms = [evs[s_][g][1].elapsed_time(evs[s_][g][2] if G > 1 else
-                                            evs[s_ + 1][g][0] if s_ + 1 < args.steps
-                                            else tail[g])
-                 for s_ in range(args.steps) for g in range(G)]
+    assign_ms = [e[0].elapsed_time(e[1]) for row in evs if row for e in row]
+    update_ms = [e[1].elapsed_time(e[2]) for row in evs if row for e in row]
     log(f"[bench] {args.steps} steps: {total_ms:.3f} ms (events), {wall * 1e3:.3f} ms (wall)")
 
     if args.copy_calibration:
@@ -326,6 +323,7 @@ def main() -> int:
             "update_algorithmic_bytes": upd_bytes,
             "update_GBps": round(upd_gbs, 1),
             "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+            "marked_steps": sum(marked),
         },
         "roofline": {
             "kernel": assign_kernel_name(fmt, d),
