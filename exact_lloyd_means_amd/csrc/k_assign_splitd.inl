@@ -34,16 +34,20 @@ constexpr int kSdRowB = 128;     // bytes of one row chunk
 constexpr int kSdSlots = kSdRowB / 16;
 constexpr int kSdStage = (kSdP + kSdK) * kSdRowB;  // LDS bytes per stage (X chunk + C chunk)
 
-// LDS byte offset of 16-byte slot s of row r inside a [rows][128 B] chunk
-__device__ inline int sd_slot(int r, int s) { return r * kSdRowB + ((s ^ (r & 7)) << 4); }
+// LDS byte offset of 16-byte slot s of row r inside a [rows][128 B] chunk.
+// Two 128-byte rows share a 256-byte line of the 64 banks (row parity picks
+// the half); XORing the slot with (r / 2) % 8 gives each of 16 consecutive
+// rows read at one slot its own 16-byte bank group, so a fragment read (16
+// lanes per pass, consecutive rows) is conflict-free.
+__device__ inline int sd_slot(int r, int s) { return r * kSdRowB + ((s ^ ((r >> 1) & 7)) << 4); }
 
 // VEC: d is a multiple of the 16-byte slot (slots load whole); else per element.
 // DMA (whole 128-byte chunks, K >= 256, each problem's rows under 4 GiB):
 // the chunks reach LDS by direct global-to-LDS loads instead of through
 // registers.  Wave w's load u fills LDS bytes [(8 u + w) KiB, +1 KiB) of the
 // stage: rows 8 (8 u + w) .. + 7, lane i taking physical slot i % 8 of row
-// (8 u + w) 8 + i / 8, i.e. the row's logical slot (i % 8) ^ (row % 8), so
-// the swizzled layout the fragment reads expect comes out of the linear
+// (8 u + w) 8 + i / 8, i.e. the row's logical slot (i % 8) ^ ((row / 2) % 8),
+// so the swizzled layout the fragment reads expect comes out of the linear
 // lane-order writes of the load.
 template <typename T, bool VEC, bool SMALLK, bool DMA>
 __global__ __launch_bounds__(kSdWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -105,7 +109,9 @@ void k_assign_splitd(const T* __restrict__ X, const T* __restrict__ C,
     static_assert(kSdP == kSdK && LPT == 8 && kSdSlots == 8, "direct-load layout");
     const uint32_t rowb = (uint32_t)d * (uint32_t)sizeof(T);
     uint32_t dma_row[LPT];  // point row (global) or centroid row within the tile
-    const uint32_t dma_slot = (uint32_t)(((lane & 7) ^ ((lane >> 3) & 7)) * 16);  // (row % 8) = lane / 8 % 8
+    // (row / 2) % 8 = (4 (wave % 2) + lane / 16) % 8: rows of load u start at
+    // a multiple of 8 rows, 8 (8 u + wave)
+    const uint32_t dma_slot = (uint32_t)(((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7)) * 16);
 #pragma unroll
     for (int u = 0; u < LPT; ++u) {
         const int r = (u * kSdWaves + wave) * 8 + (lane >> 3);
