@@ -9,20 +9,21 @@
 // Design: a workgroup of 8 waves owns 256 points of one problem and walks
 // all K centroids in tiles of 256.  For each (point block, centroid tile)
 // pair it accumulates the full dot products over d in 128-byte chunks: the
-// point chunk [256 x 128 B] and the centroid chunk [256 x 128 B] are staged
-// through registers into double-buffered LDS (16-byte slots XOR-swizzled by
-// row, so the fragment reads are conflict-free).  Wave w computes points
-// [128*(w%2), +128) x centroids [64*(w/2), +64) of the tile: 4 x 2 blocks of
-// v_mfma_f32_32x32x16_{f16,bf16} (or 32x32x2_f32), 128 accumulators per
-// lane, the centroid bias as the accumulator input of the first chunk.  After
-// the last chunk each lane folds its 2 x 16 scores per point into a running
-// (max score, lowest index); at the end the 4 waves x 2 half-waves holding
-// the same point merge lexicographically through LDS.
+// point chunk [256 x 128 B] and the centroid chunk [256 x 128 B] reach
+// double-buffered LDS (16-byte slots XOR-swizzled by row, so the fragment
+// reads are conflict-free).  Wave w computes points [128*(w%2), +128) x
+// centroids [64*(w/2), +64) of the tile: 8 x 4 blocks of
+// v_mfma_f32_16x16x32_{f16,bf16} (fp32 and register staging: 4 x 2 blocks
+// of the 32x32 forms), 128 accumulators per lane, the centroid bias as the
+// accumulators' start.  After the last chunk each lane folds its scores of every
+// point it holds into a running (max score, lowest index); at the end the
+// candidates of each point (row groups, centroid quarters) merge
+// lexicographically.
 #pragma once
 
 #include <math.h>
 
-#include "k_assign.inl"
+#include "k_assign16.inl"
 
 namespace fk {
 namespace {
@@ -131,12 +132,24 @@ void k_assign_splitd(const T* __restrict__ X, const T* __restrict__ C,
         }
     };
 
-    float best[4];
-    int32_t bidx[4];
+    // 16-bit inputs with direct loads use v_mfma_f32_16x16x32 (a quarter of
+    // the accumulator registers per instruction, which sustains more flops
+    // under the power limit than the 32x32x16 form): lane (g, c) = (lane / 16,
+    // lane % 16) holds rows 4 g + i of a 16-centroid block for point column
+    // c, so a wave's 128 x 64 scores are 8 point blocks x 4 centroid blocks
+    // and each lane keeps one running (max, index) per point block.  fp32
+    // and the register-staged forms (whose staging registers leave no room
+    // for the 16x16 fragments) keep the 32x32 form: 4 point blocks of 32,
+    // two half-waves per point.
+    constexpr bool M16 = sizeof(T) == 2 && DMA;
+    constexpr int NB = M16 ? 8 : 4;  // point blocks (running maxima) per lane
+    const int g = lane >> 4, c16 = lane & 15;
+    float best[NB];
+    int32_t bidx[NB];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-        best[cb] = -INFINITY;
-        bidx[cb] = 0;
+    for (int pb = 0; pb < NB; ++pb) {
+        best[pb] = -INFINITY;
+        bidx[pb] = 0;
     }
 
     u32x4 pre[LPT];
@@ -150,6 +163,7 @@ void k_assign_splitd(const T* __restrict__ X, const T* __restrict__ C,
             s_bias[tid] = k < K32 ? biasb[min(k, K32 - 1)] : -INFINITY;
         }
         floatx16 acc[2][4];
+        floatx4 acc16[4][8];
         if constexpr (DMA) {
             dma_chunk(kbase, 0, 0);
             wait_vm<0>();
@@ -160,18 +174,30 @@ void k_assign_splitd(const T* __restrict__ X, const T* __restrict__ C,
             for (int u = 0; u < LPT; ++u) store_slot(u, 0, pre[u]);
         }
         __syncthreads();
-        // bias vectors of this wave's two row blocks
+        // bias vectors of this wave's row blocks (the accumulators' rows)
         floatx16 bv[2];
+        if constexpr (M16) {
+            // (the accumulators start at the bias: nothing extra stays live
+            // through the chunk loop)
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            const float* sb = s_bias + wc * 64 + rb * 32 + 4 * h;
+            for (int cb = 0; cb < 4; ++cb) {
+                const floatx4 b4 =
+                    *reinterpret_cast<const floatx4*>(s_bias + wc * 64 + cb * 16 + 4 * g);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const floatx4 v4 = *reinterpret_cast<const floatx4*>(sb + 8 * g);
-                bv[rb][4 * g + 0] = v4[0];
-                bv[rb][4 * g + 1] = v4[1];
-                bv[rb][4 * g + 2] = v4[2];
-                bv[rb][4 * g + 3] = v4[3];
+                for (int pb = 0; pb < 8; ++pb) acc16[cb][pb] = b4;
+            }
+        } else {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const float* sb = s_bias + wc * 64 + rb * 32 + 4 * h;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const floatx4 v4 = *reinterpret_cast<const floatx4*>(sb + 8 * q);
+                    bv[rb][4 * q + 0] = v4[0];
+                    bv[rb][4 * q + 1] = v4[1];
+                    bv[rb][4 * q + 2] = v4[2];
+                    bv[rb][4 * q + 3] = v4[3];
+                }
             }
         }
         for (int ch = 0; ch < nch; ++ch) {
@@ -192,23 +218,48 @@ void k_assign_splitd(const T* __restrict__ X, const T* __restrict__ C,
             if constexpr (sizeof(T) == 2) __builtin_amdgcn_s_setprio(1);
             const char* xs = s_stage + buf * kSdStage;
             const char* cs = xs + kSdP * kSdRowB;
+            if constexpr (M16) {
+                // two k-steps of 32 per chunk: lane group g reads slot 4 ks + g
+                // of its 16 centroid rows (A) and 16 point rows (B)
 #pragma unroll
-            for (int s = 0; s < kSdSlots / 2; ++s) {
-                u32x4 a[2], x[4];
+                for (int ks = 0; ks < kSdSlots / 4; ++ks) {
+                    u32x4 a[4], x[8];
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
-                    a[rb] = *reinterpret_cast<const u32x4*>(cs + sd_slot(wc * 64 + rb * 32 + col, 2 * s + h));
+                    for (int cb = 0; cb < 4; ++cb)
+                        a[cb] = *reinterpret_cast<const u32x4*>(
+                            cs + sd_slot(wc * 64 + cb * 16 + c16, 4 * ks + g));
 #pragma unroll
-                for (int cb = 0; cb < 4; ++cb)
-                    x[cb] = *reinterpret_cast<const u32x4*>(xs + sd_slot(wp * 128 + cb * 32 + col, 2 * s + h));
+                    for (int pb = 0; pb < 8; ++pb)
+                        x[pb] = *reinterpret_cast<const u32x4*>(
+                            xs + sd_slot(wp * 128 + pb * 16 + c16, 4 * ks + g));
 #pragma unroll
-                for (int e = 0; e < M::kSteps; ++e)
+                    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                        for (int pb = 0; pb < 8; ++pb)
+                            acc16[cb][pb] = Mfma16<T>::step(a[cb], x[pb], acc16[cb][pb]);
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < kSdSlots / 2; ++s) {
+                    u32x4 a[2], x[4];
 #pragma unroll
                     for (int rb = 0; rb < 2; ++rb)
+                        a[rb] = *reinterpret_cast<const u32x4*>(
+                            cs + sd_slot(wc * 64 + rb * 32 + col, 2 * s + h));
 #pragma unroll
-                        for (int cb = 0; cb < 4; ++cb)
-                            acc[rb][cb] = M::step(a[rb], x[cb],
-                                                  (ch == 0 && s == 0 && e == 0) ? bv[rb] : acc[rb][cb], e);
+                    for (int cb = 0; cb < 4; ++cb)
+                        x[cb] = *reinterpret_cast<const u32x4*>(
+                            xs + sd_slot(wp * 128 + cb * 32 + col, 2 * s + h));
+#pragma unroll
+                    for (int e = 0; e < M::kSteps; ++e)
+#pragma unroll
+                        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                            for (int cb = 0; cb < 4; ++cb)
+                                acc[rb][cb] = M::step(
+                                    a[rb], x[cb],
+                                    (ch == 0 && s == 0 && e == 0) ? bv[rb] : acc[rb][cb], e);
+                }
             }
             if constexpr (sizeof(T) == 2) __builtin_amdgcn_s_setprio(0);
             if (more) {
@@ -221,38 +272,82 @@ void k_assign_splitd(const T* __restrict__ X, const T* __restrict__ C,
             }
             __syncthreads();
         }
-        // fold this tile's scores: rows ascend with (rb, r) inside a lane
+        // fold this tile's scores: rows ascend with (cb, i) (16-bit) or
+        // (rb, r) (fp32) inside a lane
+        if constexpr (M16) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            float m = best[cb];
-            int32_t rt = -1;
+            for (int pb = 0; pb < 8; ++pb) {
+                float m = best[pb];
+                int32_t rt = -1;
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+                for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float sc = acc[rb][cb][r];
-                    const bool keep = !(sc > m);
-                    m = keep ? m : sc;
-                    rt = keep ? rt : rb * 32 + 8 * (r >> 2) + (r & 3);
-                }
-            best[cb] = m;
-            bidx[cb] = rt >= 0 ? kbase + wc * 64 + rt : bidx[cb];
+                    for (int i = 0; i < 4; ++i) {
+                        const float sc = acc16[cb][pb][i];
+                        const bool keep = !(sc > m);
+                        m = keep ? m : sc;
+                        rt = keep ? rt : cb * 16 + 4 * g + i;
+                    }
+                best[pb] = m;
+                bidx[pb] = rt >= 0 ? kbase + wc * 64 + rt : bidx[pb];
+            }
+        } else {
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                float m = best[cb];
+                int32_t rt = -1;
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float sc = acc[rb][cb][r];
+                        const bool keep = !(sc > m);
+                        m = keep ? m : sc;
+                        rt = keep ? rt : rb * 32 + 8 * (r >> 2) + (r & 3);
+                    }
+                best[cb] = m;
+                bidx[cb] = rt >= 0 ? kbase + wc * 64 + rt : bidx[cb];
+            }
         }
     }
 
-    // ---- merge the 4 centroid quarters x 2 half-waves of every point
+    // ---- merge every point's candidates (lexicographic on (score, index)):
+    // 16-bit: the 4 row groups of a lane column through shuffles, then the 4
+    // centroid quarters through LDS; fp32: 4 quarters x 2 half-waves in LDS
+    constexpr int NQ = M16 ? 4 : 8;  // candidates per point in LDS
+    if constexpr (M16) {
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-        const int p = wp * 128 + cb * 32 + col;
-        s_best[(wc * 2 + h) * kSdP + p] = best[cb];
-        s_idx[(wc * 2 + h) * kSdP + p] = bidx[cb] + 4 * h;
+        for (int pb = 0; pb < 8; ++pb) {
+            float sc = best[pb];
+            int32_t ix = bidx[pb];
+#pragma unroll
+            for (int o = 16; o <= 32; o <<= 1) {
+                const float so = __shfl_xor(sc, o);
+                const int32_t io = __shfl_xor(ix, o);
+                const bool take = so > sc || (so == sc && io < ix);
+                sc = take ? so : sc;
+                ix = take ? io : ix;
+            }
+            if (g == 0) {
+                const int p = wp * 128 + pb * 16 + c16;
+                s_best[wc * kSdP + p] = sc;
+                s_idx[wc * kSdP + p] = ix;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const int p = wp * 128 + cb * 32 + col;
+            s_best[(wc * 2 + h) * kSdP + p] = best[cb];
+            s_idx[(wc * 2 + h) * kSdP + p] = bidx[cb] + 4 * h;
+        }
     }
     __syncthreads();
     if (tid < kSdP) {
         const int p = tid;
         float sc = s_best[p];
         int32_t i = s_idx[p];
-        for (int j = 1; j < 8; ++j) {
+        for (int j = 1; j < NQ; ++j) {
             const float so = s_best[j * kSdP + p];
             const int32_t io = s_idx[j * kSdP + p];
             if (so > sc || (so == sc && io < i)) {
