@@ -400,7 +400,7 @@ def run_sweep(args) -> int:
         def variant(np_, w, g=0):
             return lambda: fk.fk_assign_variant(X, Cq, bias, lab, np_, w, g)
         shapes = [((np_, w, 0), variant(np_, w)) for np_, w in itertools.product((1, 2, 4, 8),
-                                                                                   (4, 8))]
+                                                                                   (2, 4, 8))]
         # the shape fk_assign's dispatch picks (assign16_np and assign16_waves
         # in k_assign16.inl: four blocks and four waves for d <= 256), one
         # workgroup per block

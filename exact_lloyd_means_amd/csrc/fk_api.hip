@@ -636,7 +636,7 @@ fk_status fk_assign_variant(const fk_problem* p, const void* X, const void* C, c
     if (p->K < 32) return fail(FK_EUNSUPPORTED, "assign variants need K >= 32");
     if (point_blocks != 1 && point_blocks != 2 && point_blocks != 4 && point_blocks != 8)
         return fail(FK_EINVAL, "point_blocks must be 1, 2, 4 or 8");
-    if (waves != 4 && waves != 8) return fail(FK_EINVAL, "waves must be 4 or 8");
+    if (waves != 2 && waves != 4 && waves != 8) return fail(FK_EINVAL, "waves must be 2, 4 or 8");
     if (grid_wgs < 0 || grid_wgs > 0x7fffffff) return fail(FK_EINVAL, "grid_wgs out of range");
     hipStream_t s = static_cast<hipStream_t>(stream);
     FK_TRY(launch_assign_variant(X, C, bias, labels, p->B, p->N, p->K, (int)p->d, point_blocks,

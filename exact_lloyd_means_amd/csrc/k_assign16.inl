@@ -557,7 +557,9 @@ constexpr int assign16_np(int S) {
 // Waves per workgroup: four, so two workgroups share a CU, each with its
 // own LDS ring, and one workgroup's barrier waits overlap the other's
 // matrix work (eight waves, one workgroup per CU, measured 8-28 % slower
-// with four point blocks at d = 64, 128 and 256).
+// with four point blocks at d = 64, 128 and 256; two waves, four
+// workgroups per CU, each staging every centroid tile for half the points,
+// 2-11 % slower at d = 64 and 128 and 67 % at d = 256).
 constexpr int assign16_waves(int) { return 4; }
 
 // 16-bit inputs with d <= 256: S = k-steps of 32 (a power of two covering

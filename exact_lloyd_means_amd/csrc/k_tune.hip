@@ -31,6 +31,7 @@ hipError_t tune_w(int np, int waves, const void* X, const void* C, const float* 
                   int32_t* labels, int64_t B, int64_t N, int64_t K, int d, int64_t grid_wgs,
                   hipStream_t s) {
     switch (waves) {
+        case 2: return tune_np<S, 2>(np, X, C, bias, labels, B, N, K, d, grid_wgs, s);
         case 4: return tune_np<S, 4>(np, X, C, bias, labels, B, N, K, d, grid_wgs, s);
         case 8: return tune_np<S, 8>(np, X, C, bias, labels, B, N, K, d, grid_wgs, s);
         default: return hipErrorInvalidValue;

@@ -21,7 +21,7 @@ extern "C" {
 /*
  * fk_assign_variant -- fk_assign_with_bias with an explicit kernel shape:
  *   point_blocks  16-point column blocks per wave: 1, 2, 4 or 8;
- *   waves         waves per workgroup: 4 or 8;
+ *   waves         waves per workgroup: 2, 4 or 8;
  *   grid_wgs      workgroups launched (each then takes several blocks of
  *                 points in turn); 0 = one workgroup per block of points.
  * Labels are identical to fk_assign_with_bias for every shape.  fp16

@@ -26,7 +26,7 @@ def test_all_shapes_agree(d):
     fk.fk_assign_with_bias(X, C, bias, ref)
     lab = torch.empty_like(ref)
     for np_ in (1, 2, 4, 8):
-        for waves in (4, 8):
+        for waves in (2, 4, 8):
             for grid in (0, 7):
                 lab.fill_(-1)
                 fk.fk_assign_variant(X, C, bias, lab, np_, waves, grid)
