@@ -176,8 +176,12 @@ __device__ inline void clear_multi_rows(const int32_t* __restrict__ counts,
     }
 }
 
-constexpr int kPlanPer = 16;
-constexpr int kPlanBlock = kBlock * kPlanPer;  // labels per plan workgroup
+// The plan workgroup: 16 waves, 4 labels per thread (fewer serial label
+// steps per thread than 4 waves with 16 each; one workgroup is all a
+// problem with K <= 4096 gets)
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanPer = 4;
+constexpr int kPlanBlock = kPlanThreads * kPlanPer;  // labels per plan workgroup
 static_assert(kPlanBlock == kPlanLabels, "plan block size");
 
 // ---- tiled counting sort ----------------------------------------------------
@@ -220,14 +224,17 @@ __global__ __launch_bounds__(kBlock) void k_tile_hist(const int32_t* __restrict_
 
 // Column pass: th[b][t][k] <- sum_{t' < t} th[b][t'][k]; counts[b][k] and
 // bad[b] (column K) receive the column totals.  A workgroup takes 64
-// columns; the 4 waves split the tiles into 4 consecutive groups, sum their
+// columns; its G waves split the tiles into G consecutive groups, sum their
 // group, exchange the group totals through LDS and rewrite their group as a
-// running prefix.
-constexpr int kColGroups = kBlock / kWave;
-__global__ __launch_bounds__(kBlock) void k_tile_colscan(int32_t* __restrict__ th,
-                                                         int32_t* __restrict__ counts,
-                                                         int32_t* __restrict__ bad, int64_t K,
-                                                         int64_t T) {
+// running prefix.  Each wave walks its tiles in dependent batches, so many
+// tiles per problem (one problem of 2^20 points: 256 tiles) want more
+// waves per column block.
+template <int G>
+__global__ __launch_bounds__(G * kWave) void k_tile_colscan(int32_t* __restrict__ th,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ bad, int64_t K,
+                                                            int64_t T) {
+    constexpr int kColGroups = G;
     __shared__ int32_t s_tot[kColGroups][kWave];
     const int64_t b = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
@@ -324,9 +331,10 @@ __global__ __launch_bounds__(kBlock) void k_plan_totals(const int32_t* __restric
     }
 }
 
-// Inclusive scan of v over the workgroup's threads in thread order (wave
-// scans by lane shifts, then the wave totals through LDS); *total receives
-// the sum over the workgroup.  Every thread of the workgroup must call it.
+// Inclusive scan of v over the NT threads of the workgroup in thread order
+// (wave scans by lane shifts, then the wave totals through LDS); *total
+// receives the sum over the workgroup.  Every thread must call it.
+template <int NT>
 __device__ inline int32_t block_inclusive_scan(int32_t v, int32_t* __restrict__ s_w,
                                                int32_t* total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -339,7 +347,7 @@ __device__ inline int32_t block_inclusive_scan(int32_t v, int32_t* __restrict__ 
     __syncthreads();
     int32_t before = 0, all = 0;
 #pragma unroll
-    for (int q = 0; q < kBlock / kWave; ++q) {
+    for (int q = 0; q < NT / kWave; ++q) {
         const int32_t t = s_w[q];
         before += q < w ? t : 0;
         all += t;
@@ -354,12 +362,12 @@ __device__ inline int32_t block_inclusive_scan(int32_t v, int32_t* __restrict__ 
 // of the block's segments.  Thread t owns the kPlanPer consecutive labels
 // kPlanPer t .. kPlanPer t + kPlanPer - 1 of the block in registers for the
 // scans (each a scan of the per-thread totals); the results go through LDS
-// so that thread t then writes labels t, t + kBlock, ...  A segment of few
+// so that thread t then writes labels t, t + kPlanThreads, ...  A segment of few
 // pieces is written by the thread that holds it; the pieces of segments with many
 // (hot clusters) are listed, numbered with a second scan, and split evenly
 // over the threads (each walks a contiguous run of them).  The last block
 // writes the totals; block 0 of problem 0 clears the move word.
-__global__ __launch_bounds__(kBlock) void k_plan(const int32_t* __restrict__ counts,
+__global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict__ counts,
                                                  const int32_t* __restrict__ part,
                                                  int32_t* __restrict__ offsets,
                                                  int32_t* __restrict__ poff,
@@ -367,11 +375,12 @@ __global__ __launch_bounds__(kBlock) void k_plan(const int32_t* __restrict__ cou
                                                  uint32_t* __restrict__ move, int64_t K,
                                                  int64_t M) {
     constexpr int kBigPieces = 8;  // segments with more pieces go to the shared list
-    __shared__ int32_t s_w[kBlock / kWave];
+    __shared__ int32_t s_w[kPlanThreads / kWave];
     __shared__ int32_t s_base[2];
     __shared__ int32_t s_off[kPlanBlock];
     __shared__ int32_t s_po[kPlanBlock];
-    __shared__ int32_t s_big_k[kBlock], s_big_pos[kBlock], s_big_piece[kBlock], s_big_first[kBlock + 1];
+    __shared__ int32_t s_big_k[kPlanThreads], s_big_pos[kPlanThreads], s_big_piece[kPlanThreads],
+        s_big_first[kPlanThreads + 1];
     __shared__ int32_t s_nbig;
     const int64_t b = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
     const int64_t k0 = blk * kPlanBlock;
@@ -393,8 +402,8 @@ __global__ __launch_bounds__(kBlock) void k_plan(const int32_t* __restrict__ cou
     }
     // exclusive starts of this thread's labels and pieces within the block
     int32_t tot_c, tot_p;
-    const int32_t ic = block_inclusive_scan(cs, s_w, &tot_c);
-    const int32_t ip = block_inclusive_scan(ps, s_w, &tot_p);
+    const int32_t ic = block_inclusive_scan<kPlanThreads>(cs, s_w, &tot_c);
+    const int32_t ip = block_inclusive_scan<kPlanThreads>(ps, s_w, &tot_p);
     const int32_t bc = s_base[0], bp = s_base[1];
     int32_t* off = offsets + b * (K + 1);
     int32_t* po = poff + b * (K + 1);
@@ -412,7 +421,7 @@ __global__ __launch_bounds__(kBlock) void k_plan(const int32_t* __restrict__ cou
         }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += kBlock) {
+    for (int i = threadIdx.x; i < n; i += kPlanThreads) {
         const int64_t k = k0 + i;
         const int32_t o0 = s_off[i], p0 = s_po[i];
         off[k] = o0;
@@ -421,7 +430,7 @@ __global__ __launch_bounds__(kBlock) void k_plan(const int32_t* __restrict__ cou
         bool mine = pc <= kBigPieces;
         if (!mine) {
             const int32_t at = atomicAdd(&s_nbig, 1);
-            if (at < kBlock) {
+            if (at < kPlanThreads) {
                 s_big_k[at] = (int32_t)k;
                 s_big_pos[at] = o0;
                 s_big_piece[at] = p0;
@@ -444,22 +453,22 @@ __global__ __launch_bounds__(kBlock) void k_plan(const int32_t* __restrict__ cou
         }
         // unused slots: a segment-sums wave may read its slot without
         // waiting for the count
-        for (int64_t j = bp + tot_p + threadIdx.x; j < M; j += kBlock) P[1 + j] = -1;
+        for (int64_t j = bp + tot_p + threadIdx.x; j < M; j += kPlanThreads) P[1 + j] = -1;
     }
     __syncthreads();
-    const int nbig = min(s_nbig, kBlock);
+    const int nbig = min(s_nbig, kPlanThreads);
     if (nbig > 0) {
         // number the listed pieces: entry r owns flat pieces
         // s_big_first[r] .. s_big_first[r + 1] - 1
         const int32_t mine = (int)threadIdx.x < nbig ? s_big_first[threadIdx.x] : 0;
         int32_t tb;
-        const int32_t inc = block_inclusive_scan(mine, s_w, &tb);
+        const int32_t inc = block_inclusive_scan<kPlanThreads>(mine, s_w, &tb);
         if ((int)threadIdx.x < nbig) s_big_first[threadIdx.x] = inc - mine;
         if (threadIdx.x == 0) s_big_first[nbig] = tb;
         __syncthreads();
-        // thread t writes flat pieces [t tb / kBlock, (t + 1) tb / kBlock)
-        const int32_t j0 = (int32_t)((int64_t)threadIdx.x * tb / kBlock);
-        const int32_t j1 = (int32_t)((int64_t)(threadIdx.x + 1) * tb / kBlock);
+        // thread t writes flat pieces [t tb / NT, (t + 1) tb / NT)
+        const int32_t j0 = (int32_t)((int64_t)threadIdx.x * tb / kPlanThreads);
+        const int32_t j1 = (int32_t)((int64_t)(threadIdx.x + 1) * tb / kPlanThreads);
         if (j0 < j1) {
             int lo = 0, hi = nbig - 1;  // last entry whose first piece is <= j0
             while (lo < hi) {
@@ -482,6 +491,29 @@ __global__ __launch_bounds__(kBlock) void k_plan(const int32_t* __restrict__ cou
     if (b == 0 && blk == 0 && threadIdx.x == 0 && move) *move = 0u;
 }
 
+// Workgroup -> (problem b, tile t) of the scatter.  Workgroups go to the 8
+// XCDs round-robin (workgroup g to XCD g mod 8).  With pairs = B T > 0 (1-D
+// grid of 8 ceil(B T / 8) workgroups) the (b, t) pairs, problem-major, are
+// cut into 8 consecutive runs, one per XCD, so each XCD scatters
+// consecutive tiles of a problem: neighbouring tiles write neighbouring
+// positions inside every segment, so the cache lines they share are
+// completed in one L2 and written back once instead of once per XCD
+// (K = 4096 over N = 2^20 in one problem: 36 MB written for 4 MB of
+// indices with the plain order).  pairs = 0: 2-D grid (tiles, B).  Returns
+// false for the padding workgroups past the last pair.
+__device__ inline bool scatter_tile(int64_t pairs, int64_t T, int64_t& b, int64_t& t) {
+    if (pairs == 0) {
+        b = blockIdx.y;
+        t = blockIdx.x;
+        return true;
+    }
+    const int64_t run = (pairs + 7) / 8;
+    const int64_t L = (int64_t)(blockIdx.x % 8) * run + blockIdx.x / 8;
+    b = L / T;
+    t = L % T;
+    return L < pairs;
+}
+
 // Scatter of tile t: base of label k = offsets[k] + th[b][t][k].  The
 // scatter is stable: a label's points land in increasing index order.
 // Round j takes elements i0 + 256 j + tid (64 consecutive per wave); inside
@@ -494,20 +526,10 @@ __global__ __launch_bounds__(kBlock) void k_tile_scatter(
     const int32_t* __restrict__ labels, const int32_t* __restrict__ th,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_idx,
     const int32_t* __restrict__ counts, float* __restrict__ sums, int32_t* __restrict__ arrive,
-    int64_t N, int64_t K, int64_t T, int64_t d, int xcd_map, int nbits) {
+    int64_t N, int64_t K, int64_t T, int64_t d, int64_t pairs, int nbits) {
     extern __shared__ int32_t s_base[];  // [K]
-    // Workgroups go to the 8 XCDs round-robin.  With xcd_map (B a multiple
-    // of 8, 1-D grid) all tiles of problem b run on XCD b mod 8, so the
-    // partial cache lines of its sorted indices merge in one L2.
     int64_t b, t;
-    if (xcd_map) {
-        const int64_t x = blockIdx.x % 8, q = blockIdx.x / 8;
-        b = x + 8 * (q / T);
-        t = q % T;
-    } else {
-        b = blockIdx.y;
-        t = blockIdx.x;
-    }
+    if (!scatter_tile(pairs, T, b, t)) return;
     if (sums) clear_multi_rows(counts + b * K, sums + b * K * d, arrive + b * K, K, d, t, T);
     const int32_t* pre = th + (b * T + t) * (K + 1);
     const int32_t* off = offsets + b * (K + 1);
@@ -570,7 +592,7 @@ __global__ __launch_bounds__(NW * kWave) void k_tile_scatter_w(
     const int32_t* __restrict__ labels, const int32_t* __restrict__ th,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_idx,
     const int32_t* __restrict__ counts, float* __restrict__ sums, int32_t* __restrict__ arrive,
-    int64_t N, int64_t K, int64_t T, int64_t d, int xcd_map, int nbits) {
+    int64_t N, int64_t K, int64_t T, int64_t d, int64_t pairs, int nbits) {
     constexpr int kRange = kSortTile / NW;  // elements per wave
     constexpr int kPer = kRange / kWave;    // rounds per wave
     static_assert(NW % 2 == 0 && kRange % kWave == 0 && kRange < 65536, "16-bit cursors");
@@ -578,14 +600,7 @@ __global__ __launch_bounds__(NW * kWave) void k_tile_scatter_w(
     int32_t* s_base = s_mem;
     uint32_t* s_cur = reinterpret_cast<uint32_t*>(s_mem + K);
     int64_t b, t;
-    if (xcd_map) {
-        const int64_t x = blockIdx.x % 8, q = blockIdx.x / 8;
-        b = x + 8 * (q / T);
-        t = q % T;
-    } else {
-        b = blockIdx.y;
-        t = blockIdx.x;
-    }
+    if (!scatter_tile(pairs, T, b, t)) return;
     const int32_t* pre = th + (b * T + t) * (K + 1);
     const int32_t* off = offsets + b * (K + 1);
     const int lane = threadIdx.x & 63;
@@ -1463,8 +1478,13 @@ hipError_t launch_sort(const SortParams& sp, int64_t B, int64_t N, int64_t K, hi
     if (tiled) {
         hipLaunchKernelGGL(k_tile_hist, tiles, dim3(kBlock), (size_t)(K + 1) * sizeof(int32_t), s,
                            sp.labels, sp.table, N, K, T);
-        hipLaunchKernelGGL(k_tile_colscan, dim3((unsigned)((K + kWave) / kWave), (unsigned)B),
-                           dim3(kBlock), 0, s, sp.table, sp.counts, sp.bad, K, T);
+        const dim3 cgrid((unsigned)((K + kWave) / kWave), (unsigned)B);
+        if (T >= 64)
+            hipLaunchKernelGGL(k_tile_colscan<16>, cgrid, dim3(16 * kWave), 0, s, sp.table,
+                               sp.counts, sp.bad, K, T);
+        else
+            hipLaunchKernelGGL(k_tile_colscan<4>, cgrid, dim3(4 * kWave), 0, s, sp.table,
+                               sp.counts, sp.bad, K, T);
     } else {
         ZeroRanges z{};
         z.p[0] = reinterpret_cast<uint32_t*>(sp.counts);
@@ -1480,11 +1500,13 @@ hipError_t launch_sort(const SortParams& sp, int64_t B, int64_t N, int64_t K, hi
     if (nblk > 1)
         hipLaunchKernelGGL(k_plan_totals, dim3((unsigned)nblk, (unsigned)B), dim3(kBlock), 0, s,
                            sp.counts, sp.part, K);
-    hipLaunchKernelGGL(k_plan, dim3((unsigned)nblk, (unsigned)B), dim3(kBlock), 0, s, sp.counts,
+    hipLaunchKernelGGL(k_plan, dim3((unsigned)nblk, (unsigned)B), dim3(kPlanThreads), 0, s, sp.counts,
                        sp.part, sp.offsets, sp.poff, sp.pieces, sp.move, K, M);
     if (tiled) {
-        const int xcd_map = B % 8 == 0 && T * B < ((int64_t)1 << 31);
-        const dim3 sgrid = xcd_map ? dim3((unsigned)(T * B)) : tiles;
+        // consecutive tiles per XCD (scatter_tile) whenever the 1-D grid fits
+        // (nothing to merge when every problem is one tile)
+        const int64_t pairs = T > 1 && 8 * ((T * B + 7) / 8) < ((int64_t)1 << 31) ? T * B : 0;
+        const dim3 sgrid = pairs ? dim3((unsigned)(8 * ((pairs + 7) / 8))) : tiles;
         const int nbits = K > 1 ? 64 - __builtin_clzll((unsigned long long)(K - 1)) : 0;
         if (K <= kWaveBinsMax) {
             constexpr int NW = kScatterWaves;
@@ -1495,11 +1517,11 @@ hipError_t launch_sort(const SortParams& sp, int64_t B, int64_t N, int64_t K, hi
             hipLaunchKernelGGL(k_tile_scatter_w<NW>, sgrid, dim3(NW * kWave),
                                (size_t)scatter_w_lds<NW>(K), s, sp.labels, sp.table, sp.offsets,
                                sp.sorted_idx, sp.counts, sp.sums, sp.arrive, N, K, T, sp.d,
-                               xcd_map, nbits);
+                               pairs, nbits);
         } else
             hipLaunchKernelGGL(k_tile_scatter, sgrid, dim3(kBlock), (size_t)K * sizeof(int32_t), s,
                                sp.labels, sp.table, sp.offsets, sp.sorted_idx, sp.counts, sp.sums,
-                               sp.arrive, N, K, T, sp.d, xcd_map, nbits);
+                               sp.arrive, N, K, T, sp.d, pairs, nbits);
     } else {
         // LSD radix passes over 8-bit digits; pairs ping-pong between the
         // two halves of the radix buffer, the last pass writes sorted_idx

@@ -43,6 +43,23 @@ def test_sort_uniform(B, N, K):
     check_sort(lab.numpy(), K, c, o, s)
 
 
+@pytest.mark.parametrize("B,N,K", [(1, 300001, 700), (3, 300001, 4096), (1, 262145, 5000),
+                                   (2, 4096 * 64, 3)])
+def test_sort_many_tiles(B, N, K):
+    """64 or more sort tiles per problem (the wide column pass), a ragged
+    last tile, tile counts that are not a multiple of the 8 XCDs (padding
+    workgroups of the per-XCD tile runs), both tiled scatters (K <= 4096 and
+    above): the argsort must equal numpy's stable argsort exactly."""
+    g = torch.Generator().manual_seed(N + K + B)
+    j = torch.arange(1, K + 1, dtype=torch.float64)
+    p = j.pow(-1.2)
+    lab = torch.multinomial(p / p.sum(), B * N, replacement=True, generator=g).int().view(B, N)
+    c, o, s = sort_labels(lab.cuda(), K)
+    check_sort(lab.numpy(), K, c, o, s)
+    for b in range(B):
+        assert np.array_equal(s[b], np.argsort(lab[b].numpy(), kind="stable"))
+
+
 def test_sort_skewed_and_constant():
     g = torch.Generator().manual_seed(5)
     K = 4096
@@ -71,7 +88,7 @@ def run_update(X, labels, C_prev, want_lowp=True):
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("B,N,K,d", [(1, 1, 1, 1), (2, 5000, 100, 128), (1, 3000, 700, 3),
                                      (3, 2000, 50, 129), (1, 1000, 20, 1024), (1, 4097, 64, 100),
-                                     (2, 100, 300, 64)])
+                                     (2, 100, 300, 64), (1, 300001, 3000, 16)])
 def test_update_vs_oracle(dt, B, N, K, d):
     g = torch.Generator().manual_seed(B + N + K + d)
     X = torch.randn((B, N, d), generator=g).to(TORCH[dt]).cuda()
