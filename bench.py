@@ -115,6 +115,15 @@ def measured_traffic(workload: str, src_hash: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def tensor_sha256_16(t) -> str:
+    """First 16 hex digits of the SHA-256 of a CPU tensor's bytes."""
+    import numpy as np
+    a = t.contiguous().view(-1)
+    if a.element_size() == 2:
+        a = a.view(__import__("torch").int16)
+    return hashlib.sha256(np.ascontiguousarray(a.numpy()).view(np.uint8)).hexdigest()[:16]
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +187,8 @@ def main() -> int:
     log(f"[bench] generating {synth.describe(w)}")
     t = time.time()
     X_cpu, C0 = synth.make(w)
+    # the exact input bytes, so a run can be matched with a parity run
+    in_sha = {"X": tensor_sha256_16(X_cpu), "C0": tensor_sha256_16(C0)}
     log(f"[bench] generated in {time.time() - t:.1f}s; uploading")
     X = X_cpu.cuda()
     B, N, d = X.shape
@@ -314,7 +325,8 @@ def main() -> int:
         "data": "synthetic: seeded Gaussian mixture in HBM (" + synth.describe(w) + ")",
         "config": {"workload": w.name, "B": B, "N": N, "K": K, "d": d, "dtype": fmt,
                    "step": "1 Lloyd iteration (fused assign + sort-inverse update writing the "
-                           "next centroids, their rounded copy and bias)"},
+                           "next centroids, their rounded copy and bias)",
+                   "input_sha256_16": in_sha},
         "stages": {
             "assign_ms": round(a_mean, 4),
             "update_ms": round(u_mean, 4),

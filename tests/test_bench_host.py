@@ -116,3 +116,15 @@ def test_traffic_counts_only_for_the_sources_it_was_taken_on(tmp_path, monkeypat
 def test_unknown_summary_kind():
     r = run_bench("--summarize", "nonsense")
     assert r.returncode == 2
+
+
+def test_input_hash_is_the_sha256_of_the_bytes():
+    import hashlib
+
+    import numpy as np
+    import torch
+    x = torch.tensor([[1.0, -2.5], [0.25, 3.0]], dtype=torch.float16)
+    raw = np.array([0x3C00, 0xC100, 0x3400, 0x4200], dtype="<u2").tobytes()
+    assert bench.tensor_sha256_16(x) == hashlib.sha256(raw).hexdigest()[:16]
+    y = torch.tensor([1.0, 2.0], dtype=torch.float32)
+    assert bench.tensor_sha256_16(y) == hashlib.sha256(np.array([1.0, 2.0], "<f4").tobytes()).hexdigest()[:16]
