@@ -138,6 +138,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=25.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="after the timed steps, run the workload's T iterations from its "
+                         "initial centroids this many times: median iterations/s of the runs "
+                         "and label/centroid differences between them (0 skips)")
     ap.add_argument("--stage-every", type=int, default=5,
                     help="record the stage markers on every M-th timed step only")
     ap.add_argument("--groups", type=int, default=1,
@@ -299,6 +303,7 @@ def main() -> int:
     src_hash = assign_sources_hash()
 
     trace = objective_trace(fk, X, C0, fmt, w.iters)
+    reps = repeat_runs(fk, X, C0, fmt, w.iters, args.repeats) if args.repeats > 0 else None
 
     base = None
     if not args.no_baselines:
@@ -351,6 +356,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "unfused_baselines": base,
         "iterations": trace,
+        "repeated_runs": reps,
     }
     if pages_ms:
         out["baseline_context"] = f"pages: {pages_ms} ms/iter on NVIDIA H200 (FP16), not this machine"
@@ -666,6 +672,55 @@ def objective_trace(fk, X, C0, fmt, T):
         "max_cluster_count": [int(v) for v in maxc],
         "note": "objective = sum of min_dist (fp32 per point, summed in fp64) of each "
                 "iteration's assignment; max_cluster_count of the update after it",
+    }
+
+
+def repeat_runs(fk, X, C0, fmt, T, R):
+    """R runs of the workload's T iterations, each from the initial
+    centroids, with the calls of a timed step (HIP events around each whole
+    run): the median iterations/s over the runs, and how far each run's
+    final labels and centroids are from the first run's (multi-piece
+    segments add their partial sums with atomics in arrival order, so
+    centroid low bits, and through them near-tie labels, may differ)."""
+    import statistics
+
+    import torch
+
+    B, N, d = X.shape
+    K = C0.shape[1]
+    ws = fk.workspace(fk.problem(B, N, K, d, X.dtype))
+    bias = torch.empty((B, K), dtype=torch.float32, device="cuda")
+    labels = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    counts = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    rate, lab0, cen0, ldiff, cdiff = [], None, None, [], []
+    for _ in range(R):
+        C = C0.cuda().clone()
+        Cq = C.to(X.dtype).contiguous() if fmt != "f32" else C.clone()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        fk.fk_centroid_bias(Cq, bias)
+        for _ in range(T):
+            fk.fk_assign_with_bias(X, Cq, bias, labels)
+            fk.fk_update_bias(X, labels, C, C, Cq if fmt != "f32" else None, counts, bias, ws=ws)
+            if fmt == "f32":
+                Cq.copy_(C)
+        e1.record()
+        torch.cuda.synchronize()
+        rate.append(T / (e0.elapsed_time(e1) * 1e-3))
+        if lab0 is None:
+            lab0, cen0 = labels.clone(), C.clone()
+        else:
+            ldiff.append(int((labels != lab0).sum()))
+            cdiff.append(float((C - cen0).abs().max()))
+    return {
+        "runs": R, "iterations_per_run": T,
+        "median_iters_per_s": round(statistics.median(rate), 3),
+        "iters_per_s": [round(v, 3) for v in rate],
+        "labels_differing_from_run_0": ldiff,
+        "max_abs_centroid_diff_from_run_0": cdiff,
+        "note": "each run from the initial centroids, bias pass included, HIP events around "
+                "the whole run",
     }
 
 
