@@ -159,6 +159,33 @@ __device__ inline u32x4 load_chunk(const T* __restrict__ base, int64_t row, int6
     return out;
 }
 
+// The same 16 bytes read in U-byte units (U = 8, 4 or sizeof(T), dividing
+// the row stride d * sizeof(T)): for rows that are not whole 16-byte
+// chunks, where a 16-byte load would be misaligned.  A unit lies wholly
+// before or after d; units past d read as zero.
+template <typename T, int U>
+__device__ inline u32x4 load_chunk_units(const T* __restrict__ base, int64_t row, int64_t rows,
+                                         int d, int e0) {
+    constexpr int EU = U / (int)sizeof(T);  // elements per unit
+    u32x4 out = {0u, 0u, 0u, 0u};
+    if (row >= rows) return out;
+    const T* p = base + row * (int64_t)d + e0;
+    uint16_t h[8];
+    uint32_t w[4];
+    uint64_t q[2];
+#pragma unroll
+    for (int u = 0; u < 16 / U; ++u) {
+        const bool in = e0 + u * EU < d;
+        if constexpr (U == 8) q[u] = in ? *reinterpret_cast<const uint64_t*>(p + u * EU) : 0ull;
+        if constexpr (U == 4) w[u] = in ? *reinterpret_cast<const uint32_t*>(p + u * EU) : 0u;
+        if constexpr (U == 2) h[u] = in ? *reinterpret_cast<const uint16_t*>(p + u * EU) : (uint16_t)0;
+    }
+    if constexpr (U == 8) __builtin_memcpy(&out, q, 16);
+    if constexpr (U == 4) __builtin_memcpy(&out, w, 16);
+    if constexpr (U == 2) __builtin_memcpy(&out, h, 16);
+    return out;
+}
+
 // Q  = 16-byte chunks per half row (HR = Q * 16 / sizeof(T) dimensions),
 // NB = 32-point column blocks held by each wave,
 // VEC   = d is a multiple of the 16-byte chunk (rows load as whole chunks),

@@ -80,7 +80,7 @@ __device__ __forceinline__ int lds_slot(int row, int ch) {
 // the branch-free overlapping last tile are those of k_assign; the tiles
 // reach the ring by direct global-to-LDS loads when every thread moves whole
 // 16-byte chunks (DMA below), else through registers as in k_assign.
-template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK, bool MAT, int W>
+template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK, bool MAT, int W, int U = 2>
 __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* __restrict__ C,
                                               const float* __restrict__ bias,
                                               int32_t* __restrict__ labels,
@@ -107,6 +107,12 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
     constexpr int kBiasSlot = kSlots > 3 ? kSlots - 3 : 0;
     constexpr int kEpiSteps = 12 * NP;                 // epilogue steps per tile (epi_op)
     static_assert(!EXACT || VEC, "EXACT implies VEC");
+    // Rows that are not whole 16-byte chunks (!VEC) load in U-byte units,
+    // the widest dividing the row stride (8 or 4 bytes; U = 2: element by
+    // element); centroid units past d are read at the row's last unit
+    // instead (the points are zero there, so any finite value does).
+    constexpr bool UNITS = !VEC && !SMALLK && U >= 4;
+    constexpr int NU = 16 / U, EU = U / (int)sizeof(T);  // units per chunk, elements per unit
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* s_tile = smem;                                                      // [ring][TILEB]
@@ -149,6 +155,16 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
             goff[u] = (uint32_t)((row * d + eofs) * (int)sizeof(T));
         }
     }
+    // UNITS: byte offsets (within a tile) of the units of this thread's chunks
+    uint32_t uoff[UNITS ? PER : 1][UNITS ? NU : 1];
+    if constexpr (UNITS) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u)
+#pragma unroll
+            for (int h = 0; h < NU; ++h)
+                uoff[u][h] = (uint32_t)((crow[u] * d + min(ccol[u] * V + h * EU, d - EU)) *
+                                        (int)sizeof(T));
+    }
     // LDS byte offset (within a tile, row block 0) of the fragment of k-step
     // s this lane reads: row col, chunk 4 s + g, one register per k-step
     uint32_t faddr[S];
@@ -177,8 +193,10 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
         for (int np = 0; np < NP; ++np) {
 #pragma unroll
             for (int s = 0; s < S; ++s)
-                xf[np][s] = load_chunk<T, VEC>(X + b * N * d, pbase + np * 16 + col, N, d,
-                                               32 * s + 8 * g);
+                xf[np][s] = UNITS ? load_chunk_units<T, UNITS ? U : 8>(
+                                        X + b * N * d, pbase + np * 16 + col, N, d, 32 * s + 8 * g)
+                                  : load_chunk<T, VEC>(X + b * N * d, pbase + np * 16 + col, N, d,
+                                                       32 * s + 8 * g);
             best[np] = -INFINITY;
             bidx[np] = 0;
         }
@@ -189,7 +207,21 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
 #pragma unroll
             for (int u = 0; u < PER; ++u) {
                 if (CHUNKS % NT == 0 || CHUNKS < NT || u * NT + tid < CHUNKS) {
-                    if constexpr (SMALLK || !VEC) {
+                    if constexpr (UNITS) {
+                        uint64_t q[2];
+                        uint32_t w[4];
+#pragma unroll
+                        for (int h = 0; h < NU; ++h) {
+                            if constexpr (U == 8)
+                                q[h] = *reinterpret_cast<const uint64_t*>(base + uoff[u][h]);
+                            else
+                                w[h] = *reinterpret_cast<const uint32_t*>(base + uoff[u][h]);
+                        }
+                        if constexpr (U == 8)
+                            __builtin_memcpy(&st.v[u], q, 16);
+                        else
+                            __builtin_memcpy(&st.v[u], w, 16);
+                    } else if constexpr (SMALLK || !VEC) {
                         st.v[u] = load_chunk<T, VEC>(Cb, tbase + crow[u], K, d, ccol[u] * V);
                     } else {
                         st.v[u] = *reinterpret_cast<const u32x4*>(base + goff[u]);
@@ -476,13 +508,14 @@ __device__ __forceinline__ void assign16_body(const T* __restrict__ X, const T* 
     }
 }
 
-template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK, int W = kAssignWaves>
+template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK, int W = kAssignWaves,
+          int U = 2>
 __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_assign16(const T* __restrict__ X, const T* __restrict__ C, const float* __restrict__ bias,
                 int32_t* __restrict__ labels, float* __restrict__ min_dist, int64_t B, int64_t N,
                 int64_t K, int d) {
-    assign16_body<T, S, NP, VEC, EXACT, SMALLK, false, W>(X, C, bias, labels, min_dist, B, N, K,
-                                                          d, nullptr);
+    assign16_body<T, S, NP, VEC, EXACT, SMALLK, false, W, U>(X, C, bias, labels, min_dist, B, N,
+                                                             K, d, nullptr);
 }
 
 // The same contraction writing every score (MAT) instead of the argmax.
@@ -497,7 +530,7 @@ void k_scores16(const T* __restrict__ X, const T* __restrict__ C, const float* _
 // Launch of one instantiation.  W = waves per workgroup; grid_wgs > 0 caps
 // the grid at that many workgroups (each then loops over several items).
 template <typename T, int S, int NP, bool VEC, bool EXACT, bool SMALLK, bool MAT = false,
-          int W = kAssignWaves>
+          int W = kAssignWaves, int U = 2>
 hipError_t launch_assign16_t(const void* X, const void* C, const float* bias, int32_t* labels,
                              float* min_dist, int64_t B, int64_t N, int64_t K, int d,
                              hipStream_t s, float* D = nullptr, int64_t grid_wgs = 0) {
@@ -511,7 +544,7 @@ hipError_t launch_assign16_t(const void* X, const void* C, const float* bias, in
     if constexpr (MAT)
         kern = reinterpret_cast<const void*>(k_scores16<T, S, NP, VEC, EXACT, SMALLK>);
     else
-        kern = reinterpret_cast<const void*>(k_assign16<T, S, NP, VEC, EXACT, SMALLK, W>);
+        kern = reinterpret_cast<const void*>(k_assign16<T, S, NP, VEC, EXACT, SMALLK, W, U>);
     static LdsAttr attr;
     hipError_t e = ensure_lds(attr, kern, lds);
     if (e != hipSuccess) return e;
@@ -522,7 +555,7 @@ hipError_t launch_assign16_t(const void* X, const void* C, const float* bias, in
                            dim3(kAssignWaves * kWave), lds, s, static_cast<const T*>(X),
                            static_cast<const T*>(C), bias, D, B, N, K, d);
     else
-        hipLaunchKernelGGL((k_assign16<T, S, NP, VEC, EXACT, SMALLK, W>), grid, dim3(W * kWave),
+        hipLaunchKernelGGL((k_assign16<T, S, NP, VEC, EXACT, SMALLK, W, U>), grid, dim3(W * kWave),
                            lds, s, static_cast<const T*>(X), static_cast<const T*>(C), bias,
                            labels, min_dist, B, N, K, d);
     return hipGetLastError();
@@ -584,7 +617,13 @@ hipError_t dispatch_assign16(const void* X, const void* C, const float* bias, in
         if (vec)                                                                               \
             return launch_assign16_t<T, SS, NPP, true, false, false, false, WW>(               \
                 X, C, bias, labels, min_dist, B, N, K, d, s);                                  \
-        return launch_assign16_t<T, SS, NPP, false, false, false, false, WW>(                  \
+        if (d % 4 == 0)                                                                        \
+            return launch_assign16_t<T, SS, NPP, false, false, false, false, WW, 8>(           \
+                X, C, bias, labels, min_dist, B, N, K, d, s);                                  \
+        if (d % 2 == 0)                                                                        \
+            return launch_assign16_t<T, SS, NPP, false, false, false, false, WW, 4>(           \
+                X, C, bias, labels, min_dist, B, N, K, d, s);                                  \
+        return launch_assign16_t<T, SS, NPP, false, false, false, false, WW, 2>(               \
             X, C, bias, labels, min_dist, B, N, K, d, s);                                      \
     }
     FK_ASSIGN16_CASE(1)
