@@ -50,7 +50,10 @@ __device__ inline int sd_slot(int r, int s) { return r * kSdRowB + ((s ^ ((r >> 
 // (8 u + w) 8 + i / 8, i.e. the row's logical slot (i % 8) ^ ((row / 2) % 8),
 // so the swizzled layout the fragment reads expect comes out of the linear
 // lane-order writes of the load.
-template <typename T, bool VEC, bool SMALLK, bool DMA>
+// U (rows that are not whole slots, !VEC): 8 or 4 = rows read in units of
+// that many bytes (the widest dividing the row stride); 0 = element by
+// element.
+template <typename T, bool VEC, bool SMALLK, bool DMA, int U = 0>
 __global__ __launch_bounds__(kSdWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_assign_splitd(const T* __restrict__ X, const T* __restrict__ C,
                      const float* __restrict__ bias, int32_t* __restrict__ labels,
@@ -92,12 +95,18 @@ void k_assign_splitd(const T* __restrict__ X, const T* __restrict__ C,
         const int r = g / kSdSlots;
         const int sl = g % kSdSlots;
         const int e0 = ch * EC + sl * V;
+        auto ld = [&](const T* base, int row, int64_t rows) -> u32x4 {
+            if constexpr (!VEC && U > 0)
+                return load_chunk_units<T, U>(base, row, rows, d, e0);
+            else
+                return load_chunk<T, VEC>(base, row, rows, d, e0);
+        };
         if (r < kSdP) {
             const int row = min((int)p0 + r, N32 - 1);  // rows past N: any finite data
-            return load_chunk<T, VEC>(Xb, row, N, d, e0);
+            return ld(Xb, row, N);
         }
         const int k = kbase + (r - kSdP);
-        return load_chunk<T, VEC>(Cb, SMALLK ? k : min(k, K32 - 1), K, d, e0);
+        return ld(Cb, SMALLK ? k : min(k, K32 - 1), K);
     };
     auto store_slot = [&](int u, int buf, u32x4 v) {
         const int g = u * NT + tid;
@@ -386,13 +395,22 @@ hipError_t launch_assign_splitd(const void* X, const void* C, const float* bias,
     // direct loads: whole chunks, full tiles, 32-bit byte offsets per problem
     const bool dma = d % EC == 0 && K >= kSdK && N * (int64_t)d * (int64_t)sizeof(T) < ((int64_t)1 << 32) &&
                      K * (int64_t)d * (int64_t)sizeof(T) < ((int64_t)1 << 32);
-    const int variant = dma ? 4 : (K < kSdK ? 1 : 0) + (d % V == 0 ? 2 : 0);
+    // rows that are not whole slots: the widest load unit dividing the stride
+    const int unit = d % (8 / (int)sizeof(T)) == 0 ? 8 : (sizeof(T) == 2 && d % 2 == 0 ? 4 : 0);
+    const int smallk = K < kSdK ? 1 : 0;
+    const int variant = dma            ? 4
+                        : d % V == 0   ? 2 + smallk
+                        : unit == 8    ? 5 + smallk
+                        : unit == 4    ? 7 + smallk
+                                       : smallk;
     using Kern = void (*)(const T*, const T*, const float*, int32_t*, float*, int64_t, int64_t, int);
-    const Kern kerns[5] = {k_assign_splitd<T, false, false, false>, k_assign_splitd<T, false, true, false>,
+    const Kern kerns[9] = {k_assign_splitd<T, false, false, false>, k_assign_splitd<T, false, true, false>,
                            k_assign_splitd<T, true, false, false>, k_assign_splitd<T, true, true, false>,
-                           k_assign_splitd<T, true, false, true>};
+                           k_assign_splitd<T, true, false, true>,
+                           k_assign_splitd<T, false, false, false, 8>, k_assign_splitd<T, false, true, false, 8>,
+                           k_assign_splitd<T, false, false, false, 4>, k_assign_splitd<T, false, true, false, 4>};
     const Kern kern = kerns[variant];
-    static LdsAttr attr[5];
+    static LdsAttr attr[9];
     hipError_t e = ensure_lds(attr[variant], reinterpret_cast<const void*>(kern), (int)lds);
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)((N + kSdP - 1) / kSdP), (unsigned)B);
