@@ -103,7 +103,7 @@ EDGE = [(1, 1, 1, 1), (1, 31, 2, 2), (2, 33, 31, 3), (1, 257, 33, 8), (3, 1000, 
         (1, 200, 70, 200), (1, 130, 40, 256), (1, 100, 35, 300), (1, 70, 33, 512),
         # row strides of 8 or 4 bytes (rows loaded in 8- or 4-byte units)
         (1, 300, 70, 98), (2, 200, 90, 100), (1, 120, 260, 258), (1, 300, 64, 20),
-        (2, 100, 40, 6),
+        (2, 100, 40, 6), (1, 250, 130, 228), (1, 250, 130, 250), (2, 300, 97, 196),
         # rows longer than the register-resident limit: split-d kernel
         (1, 300, 70, 513), (2, 257, 300, 1024), (1, 100, 40, 1000), (1, 64, 33, 1100),
         (1, 150, 300, 516),
