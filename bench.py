@@ -99,7 +99,8 @@ def assign_kernel_name(fmt: str, d: int) -> str:
     element type and dimension."""
     if fmt == "f32":
         return "k_assign (fp32 32x32x2 MFMA)" if d <= 128 else "k_assign_splitd (fp32)"
-    return "k_assign16 (16x16x32 MFMA)" if d <= 256 else "k_assign_splitd (16-bit)"
+    resident = d <= 128 or (d <= 256 and d % 8 == 0)
+    return "k_assign16 (16x16x32 MFMA)" if resident else "k_assign_splitd (16-bit)"
 
 
 def measured_traffic(workload: str, src_hash: str):

@@ -595,6 +595,15 @@ constexpr int assign16_np(int S) {
 // 2-11 % slower at d = 64 and 128 and 67 % at d = 256).
 constexpr int assign16_waves(int) { return 4; }
 
+// Whether 16-bit rows of d dimensions take the register-resident kernel:
+// up to 256 dimensions in whole 16-byte chunks, or up to 128 otherwise.
+// Rows of 129-256 dimensions that are not whole chunks need eight k-steps
+// of point fragments plus the unit offsets of the staged tiles, which spill
+// about 900 bytes per lane; the split-d kernel, which keeps no point rows
+// in registers, runs them 2.4-3.2 times faster (B=8, N=65536, K=1024, same
+// labels: d = 228 fp16 1.230 -> 0.402 ms, d = 129 fp16 1.907 -> 0.649 ms).
+constexpr bool assign16_resident(int d) { return d <= 128 || (d <= 256 && d % 8 == 0); }
+
 // 16-bit inputs with d <= 256: S = k-steps of 32 (a power of two covering
 // d), assign16_np(S) 16-point blocks per wave, assign16_waves(S) waves.
 template <typename T>
