@@ -726,15 +726,22 @@ def repeat_runs(fk, X, C0, fmt, T, R):
 
 
 def host_cpu_model() -> str:
-    """The host CPU's model name (as lscpu prints it), from /proc/cpuinfo."""
+    """The host CPU's model name (as lscpu prints it), with its family,
+    model and stepping numbers (a virtual machine may report only a generic
+    name), from /proc/cpuinfo."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for ln in f:
-                if ln.startswith("model name"):
-                    return ln.split(":", 1)[1].strip()
+                if not ln.strip():
+                    break  # first processor only
+                k, _, v = ln.partition(":")
+                fields[k.strip()] = v.strip()
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = fields.get("model name", "unknown")
+    ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 def run_cpu_baseline(w, X_cpu, Cq, fmt, target_s, gpu_value):
