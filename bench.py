@@ -163,7 +163,8 @@ def main() -> int:
                     help="also run a plain 1 GiB -> 1 GiB copy kernel (PMC byte-counter calibration)")
     ap.add_argument("--summarize", nargs="+", metavar="ARG",
                     help="no GPU work: 'stats CSV CMD' prints a kernel-time summary; "
-                         "'traffic FETCH_CSV WRITE_CSV WORKLOAD CMD' writes the assign traffic record")
+                         "'traffic FETCH_CSV WRITE_CSV WORKLOAD CMD' writes the assign traffic record; "
+                         "'timed TRACE_CSV KERNEL N' averages the last N dispatches of a kernel")
     args = ap.parse_args()
     if args.summarize:
         return summarize(args.summarize)
@@ -854,6 +855,16 @@ def summarize(argv) -> int:
             print(f"| {_short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                   f"{float(r['Percentage']):.2f} |")
+        return 0
+    if kind == "timed":
+        # the last n dispatches of one kernel in a --kernel-trace CSV: those
+        # of the timed steps, which bench.py runs after its untimed runs
+        path, sub, n = argv[1], argv[2], int(argv[3])
+        rows = [r for r in csv.DictReader(open(path)) if sub in r["Kernel_Name"]]
+        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+        us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows[-n:]]
+        print(f"- {_short_name(rows[-1]['Kernel_Name'])} over the last {len(us)} dispatches "
+              f"(the timed steps): {sum(us) / len(us):.1f} us average, {min(us):.1f}-{max(us):.1f} us")
         return 0
     if kind == "traffic":
         fetch_csv, write_csv, workload, cmd = argv[1], argv[2], argv[3], " ".join(argv[4:])
